@@ -1,0 +1,172 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA absorbed-decode step on one MI355X.
+
+A step is the whole hot path for one new token per sequence:
+  mla_append_latent (the B new rows) -> mla_absorb_q -> mla_decode_paged
+  (plan + split attention + LSE combine) -> mla_out_proj,
+on the DeepSeek-V3-shaped workload (B=64, H=128, d_c=512, d_rope=64,
+d_nope=d_v=128, S=8192, page 64, bf16 latent cache, permuted pages), with all
+inputs resident in HBM.  The cache holds S-1 tokens per sequence before the
+timed region; every step appends token S-1 (the same slot each step) and
+attends over all S tokens.
+
+Prints one JSON line: whole-step decode tokens/s, plus
+  roofline: the split-attention kernel's achieved HBM bandwidth
+            (algorithmic bytes per launch / its mean duration, HIP events on
+            the launch stream) against 8 TB/s,
+  cpu_baseline: the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode tokens/s + achieved TB/s & % roofline, B=64 S=8192 H=128"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v3", choices=["v3", "v2lite", "ragged", "fp8long"])
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=2,
+                    help="sequences of the workload the oracle decodes for cpu_baseline (0 = skip)")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, n_seq: int):
+    """Time the oracle (explicit fp64 form) on the first n_seq sequences."""
+    import numpy as np
+    from oracle import reference_decode
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    reference_decode(inp, batches=range(n_seq))
+    dt = time.perf_counter() - t0
+    toks = int(np.sum(inp.seq_lens[:n_seq]))
+    return {"value": n_seq / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_seq} of {len(inp.seq_lens)} sequences x {inp.wl.n_heads} heads "
+                      f"({toks} cached tokens), explicit fp64 form, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; the decode path shards by sequence "
+              "(attention data parallel) and needs no collective, but multi-GPU runs are not "
+              "part of it. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_nope_amd as mla
+    from workload import configs, make_inputs
+    from workload.torch_io import to_device
+
+    wl = configs.get(args.workload)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = make_inputs(wl)
+    d = mla.make_dims(wl.n_heads, wl.d_c, wl.d_rope, wl.d_nope, wl.d_v, wl.page_size, fp8=wl.fp8,
+                      softmax_scale=wl.softmax_scale, rope_base=wl.rope_base)
+    t = to_device(inp, dev)
+    B, H = wl.batch, wl.n_heads
+    R = wl.d_c + wl.d_rope
+
+    # cache: every token but the last of each sequence
+    cu = inp.cu_seqlens
+    last = (cu[1:] - 1).astype(np.int64)
+    keep = np.ones(inp.total_tokens, bool)
+    keep[last] = False
+    idx_keep = torch.from_numpy(np.nonzero(keep)[0]).to(dev)
+    idx_last = torch.from_numpy(last).to(dev)
+    pool, scales = mla.new_pool(d, inp.num_pages, dev)
+    mla.append_latent(d, t["c_kv"][idx_keep].contiguous(), t["k_pe"][idx_keep].contiguous(),
+                      t["positions"][idx_keep].contiguous(), t["seq_ids"][idx_keep].contiguous(),
+                      t["block_table"], pool, scales)
+    new_c = t["c_kv"][idx_last].contiguous()
+    new_k = t["k_pe"][idx_last].contiguous()
+    new_pos = t["positions"][idx_last].contiguous()
+    new_sid = t["seq_ids"][idx_last].contiguous()
+    del t["c_kv"], t["k_pe"]
+
+    ws = mla.new_workspace(d, B, args.num_splits, dev)
+    q = torch.empty((B, H, R), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((B, H, wl.d_c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, wl.d_v), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        mla.append_latent(d, new_c, new_k, new_pos, new_sid, t["block_table"], pool, scales)
+        mla.absorb_q(d, t["q_nope"], t["q_pe"], t["q_pos"], t["w_uk"], q)
+        mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], args.num_splits,
+                         ws, o_lat, lse)
+        mla.out_proj(d, o_lat, t["w_uv"], out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mla.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    split_ms_total, n_rec = mla.profile_end()
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+
+    ms_step = 1e3 * elapsed / args.steps
+    value = B * args.steps / elapsed
+    total_tokens = int(inp.total_tokens)
+    bpt = mla.cache_bytes_per_token(d)
+    split_bytes = total_tokens * bpt + B * H * R * 2          # cache rows + the absorbed query
+    flops = 2.0 * total_tokens * H * (R + wl.d_c)             # QK^T + PV
+    split_ms = split_ms_total / max(1, n_rec)
+    achieved_gbs = split_bytes / (split_ms * 1e-3) / 1e9
+    tflops = flops / (split_ms * 1e-3) / 1e12
+    bound = "mfma" if wl.fp8 else "hbm"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "k_split (split-KV attention)", "mean_launch_ms": round(split_ms, 5),
+                 "launches": n_rec, "algorithmic_bytes_per_launch": split_bytes,
+                 "flops_per_launch": flops, "achieved_tflops": round(tflops, 1)})
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.description, "batch": B, "heads": H, "d_c": wl.d_c,
+                   "d_rope": wl.d_rope, "seq_len": wl.max_seq_len, "total_tokens": total_tokens,
+                   "page_size": wl.page_size, "cache": "fp8_e4m3" if wl.fp8 else "bf16",
+                   "num_splits": args.num_splits or "auto",
+                   "step": "append+absorb+decode(plan,split,combine)+out_proj"},
+        "decode_kernel_tokens_per_s": round(B / (split_ms * 1e-3), 1),
+        "roofline": roof,
+    }
+    if args.cpu_sample > 0:
+        rec["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample, B))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

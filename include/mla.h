@@ -1,0 +1,214 @@
+/*
+ * mla.h - C ABI of libmla: Multi-head Latent Attention (MLA) decode with the
+ * up-projections absorbed, over a paged latent cache, for AMD MI355X (gfx950).
+ *
+ * The method (as stated on the source pages):
+ *   - Only the low-rank joint latent c_kv (width d_c) of each token is cached;
+ *     per-head K and V are what c_kv becomes through the up-projections W_UK
+ *     and W_UV.  ("DeepSeek-V2拆解：MLA与MoE如何把KV缓存压降93.3%",
+ *     sheratonhq.com, section 2.1.)
+ *   - W_UK can be absorbed on the query side and W_UV on the output side, so K
+ *     and V are never materialised (same page, section 2.1; "LLM推理优化的新范式：
+ *     从内存墙到计算墙的跨越", zskr.cn, section 2.2: reordering by associativity).
+ *   - Position information travels in a separate decoupled-RoPE branch
+ *     (sheratonhq.com section 2.1; zskr.cn section 2.1): a d_rope-wide rotated
+ *     key shared by all heads, and a per-head rotated query part.
+ *   - The new token's latent is appended to the cache before attention reads it
+ *     (sheratonhq.com section 2.1, the compression sketch appends then returns).
+ *   - The cache is paged with a block size (fsdata.site "DeepSeek V3 MLA",
+ *     section 3.1: block_size=16, PagedAttention adapted to the latent space)
+ *     and may be stored in fp8 (zskr.cn section 5; fsdata.site section 3.1).
+ *
+ * Conventions used by every call:
+ *   - All array pointers are DEVICE pointers to dense row-major buffers owned
+ *     by the caller; shapes are given as [dim0][dim1]...  bf16 means the
+ *     16-bit bfloat16 format.  The library keeps no pointer after a call.
+ *   - Each call only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *     default stream).  It never synchronises and never allocates device
+ *     memory (mla_decode_paged takes a caller-provided workspace).
+ *   - Host-visible arguments are validated before anything is enqueued; a
+ *     failed check returns MLA_ERR_INVALID_ARG / MLA_ERR_UNSUPPORTED /
+ *     MLA_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
+ *     MLA_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Values that live on the device (seq_lens, block-table entries,
+ *     positions, seq_ids) are not checked on the host.  Kernels treat
+ *     out-of-range values defensively instead of faulting: a page id outside
+ *     [0, num_pages) or a position beyond the block table is skipped (its
+ *     token is neither written nor attended to) and seq_lens are clamped to
+ *     [0, max_pages * page_size].  Results for such inputs are unspecified.
+ *   - Outputs must not alias inputs.  Calls on different streams that write
+ *     the same buffers race.
+ *
+ * Cached row layout (one per token, per layer): elements [0, d_c) hold c_kv,
+ * elements [d_c, d_c + d_rope) hold k_pe already rotated at the token's
+ * position.  Pool: [num_pages][page_size][d_c + d_rope] of bf16, or of uint8
+ * E4M3FN codes plus a scale array [num_pages][page_size] of fp32.  Token t of
+ * sequence b lives in row (block_table[b][t / page_size], t % page_size).
+ *
+ * RoPE (a reading; the pages only name the decoupled branch): RoFormer's
+ * rotation of consecutive pairs (2i, 2i+1) by angle pos * rope_base^(-2i/d_rope);
+ * the angle and its sine and cosine are evaluated in fp64.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, misalignment, bad flag */
+  MLA_ERR_UNSUPPORTED = 2,   /* dimensions outside the compiled instantiations */
+  MLA_ERR_WORKSPACE = 3,     /* workspace smaller than mla_decode_workspace_size() */
+  MLA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} mla_status_t;
+
+typedef enum {
+  MLA_CACHE_BF16 = 0,        /* bf16 rows */
+  MLA_CACHE_FP8_E4M3 = 1     /* OCP E4M3FN codes + one fp32 scale per token */
+} mla_cache_dtype_t;
+
+/* Model dimensions, passed by pointer to every call (40 bytes, no padding).
+ * Supported: (d_c, d_rope, d_nope, d_v) in {(512, 64, 128, 128), (32, 16, 16, 16)};
+ * 1 <= n_heads <= 128; page_size a power of two in [16, 256]. */
+typedef struct {
+  int32_t n_heads;           /* H: query heads */
+  int32_t d_c;               /* latent width (c_kv) */
+  int32_t d_rope;            /* decoupled RoPE width (q_pe, k_pe); even */
+  int32_t d_nope;            /* per-head non-positional query/key width */
+  int32_t d_v;               /* per-head value width */
+  int32_t page_size;         /* tokens per cache page */
+  int32_t cache_dtype;       /* mla_cache_dtype_t */
+  float softmax_scale;       /* multiplies the whole score, e.g. 1/sqrt(d_nope + d_rope) */
+  double rope_base;          /* RoPE base, e.g. 10000 */
+} mla_dims_t;
+
+/* Append flag: store k_pe as given (no rotation).  Used to test placement. */
+#define MLA_APPEND_NO_ROPE 1u
+
+/*
+ * mla_append_latent - write n_tokens new latent rows into the paged cache.
+ * Source: the cache keeps only the latent, appended token by token before use
+ * (sheratonhq.com section 2.1); the RoPE key is computed once per token in its
+ * own branch (same section), so it is rotated here and stored rotated.
+ *
+ *   c_kv        bf16 [n_tokens][d_c]
+ *   k_pe        bf16 [n_tokens][d_rope], un-rotated
+ *   positions   int32 [n_tokens]: position of each token in its sequence; it
+ *               selects the slot and is the RoPE position
+ *   seq_ids     int32 [n_tokens]: row of block_table owning each token
+ *   block_table int32 [num_seqs][max_pages]
+ *   num_pages   pages in the pool
+ *   pool        bf16 or uint8 [num_pages][page_size][d_c + d_rope] (written)
+ *   scales      fp32 [num_pages][page_size] (fp8 cache only, else NULL; written)
+ *   flags       0 or MLA_APPEND_NO_ROPE
+ * Each row is (c_kv || RoPE(k_pe, position)) rounded to bf16.  For the fp8
+ * cache the row is formed in fp32 (the rotation rounded from fp64 to fp32),
+ * scale = absmax(row) / 448 (an fp32 division), and each code is the E4M3FN
+ * value nearest to row[i] / scale (ties to even, clamped to +-448); a row of
+ * zeros stores scale 0 and zero codes.  Two tokens that map to the same slot
+ * race.  n_tokens == 0 is a no-op.
+ */
+mla_status_t mla_append_latent(const mla_dims_t* dims, const void* c_kv, const void* k_pe,
+                               const int32_t* positions, const int32_t* seq_ids,
+                               const int32_t* block_table, int32_t num_seqs, int32_t max_pages,
+                               int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
+                               uint32_t flags, void* stream);
+
+/*
+ * mla_absorb_q - fold W_UK into the query and rotate the RoPE query part.
+ * Source: W_UK is absorbed into the query projection (sheratonhq.com section
+ * 2.1); the reordered path multiplies Q by the up-projection weight before
+ * scoring against the compressed cache (zskr.cn sections 2.1-2.2, and the
+ * fused Q x W_DK kernel named in section 4.2).
+ *
+ *   q_nope  bf16 [B][H][d_nope]
+ *   q_pe    bf16 [B][H][d_rope], un-rotated
+ *   q_pos   int32 [B]: query position (the last cached position, seq_len - 1)
+ *   w_uk    bf16 [H][d_c][d_nope]: K_h = C . W_UK[h]
+ *   q_out   bf16 [B][H][d_c + d_rope] (written):
+ *             q_out[b][h][0:d_c]   = W_UK[h] . q_nope[b][h]   (fp32 accumulate)
+ *             q_out[b][h][d_c:]    = RoPE(q_pe[b][h], q_pos[b])
+ */
+mla_status_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
+                          const int32_t* q_pos, const void* w_uk, int32_t B, void* q_out,
+                          void* stream);
+
+/*
+ * mla_decode_workspace_size - bytes of device workspace mla_decode_paged needs
+ * for this batch size and split count (num_splits as in mla_decode_paged).
+ * Returns 0 for unsupported dims or B <= 0.
+ */
+size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t B, int32_t num_splits);
+
+/*
+ * mla_decode_paged - single-query softmax attention of every head over its
+ * sequence's cached latent rows; the latent is used as V.
+ * Source: the core of MLA decode in the absorbed form (sheratonhq.com section
+ * 2.1; zskr.cn section 2.2); bandwidth-bound on reading the latent cache
+ * (fsdata.site section 6, decode bandwidth should approach the peak).
+ *
+ *   q           bf16 [B][H][d_c + d_rope] from mla_absorb_q
+ *   pool        cache as written by mla_append_latent; scales for fp8 else NULL
+ *   block_table int32 [B][max_pages]
+ *   seq_lens    int32 [B]: tokens of each sequence (0 allowed)
+ *   num_splits  number of equal shares the batch's tokens are cut into, each
+ *               processed by one workgroup (a share may span sequences, a
+ *               sequence may span shares); 0 = automatic (fills the GPU)
+ *   workspace   device buffer of at least mla_decode_workspace_size() bytes,
+ *               256-byte aligned; contents need no initialisation
+ *   o_lat       bf16 [B][H][d_c] (written): sum_t p_t c_kv[t]
+ *   lse         fp32 [B][H] natural-log normaliser of the scores, or NULL
+ * with s_t = softmax_scale * (q[b][h] . row_t) over t < seq_lens[b] and
+ * p = softmax(s).  A sequence of length 0 yields o_lat = 0 and lse = -inf.
+ * Results differ between split counts only by floating-point rounding.
+ */
+mla_status_t mla_decode_paged(const mla_dims_t* dims, const void* q, const void* pool,
+                              const float* scales, const int32_t* block_table, int32_t max_pages,
+                              int32_t num_pages, const int32_t* seq_lens, int32_t B,
+                              int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
+                              float* lse, void* stream);
+
+/*
+ * mla_out_proj - apply W_UV on the output side.
+ * Source: W_UV is absorbed into the output projection (sheratonhq.com section 2.1).
+ *
+ *   o_lat  bf16 [B][H][d_c]
+ *   w_uv   bf16 [H][d_c][d_v]: V_h = C . W_UV[h]
+ *   out    bf16 [B][H][d_v] (written): out[b][h] = W_UV[h]^T . o_lat[b][h] (fp32 accumulate)
+ */
+mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv, int32_t B,
+                          void* out, void* stream);
+
+/*
+ * mla_cache_bytes_per_token - bytes one token occupies in one layer's cache:
+ * 2 (d_c + d_rope) for bf16, (d_c + d_rope) + 4 for fp8 plus its scale.
+ * Source: MHA caches 2 n_h d_h elements per token per layer, MLA only the
+ * latent (sheratonhq.com sections 2.1 and 4.2); here plus the RoPE key.
+ * Returns 0 for a NULL or invalid dims.
+ */
+size_t mla_cache_bytes_per_token(const mla_dims_t* dims);
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(mla_status_t status);
+
+/*
+ * Kernel timing hooks for benchmarks (not part of the method).
+ * mla_profile_begin(n) creates n pairs of HIP events; while active, each
+ * mla_decode_paged call records one pair around its main attention kernel on
+ * its stream.  mla_profile_end() waits for the recorded events, writes the
+ * summed duration in milliseconds and the number of recorded launches, and
+ * releases the events.  Not thread-safe; for single-threaded benchmarks only.
+ */
+mla_status_t mla_profile_begin(int32_t max_records);
+mla_status_t mla_profile_end(double* total_ms, int32_t* n_records);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

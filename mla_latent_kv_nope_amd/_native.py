@@ -1,0 +1,79 @@
+"""Loads libmla.so (built in-tree by mla_latent_kv_nope_amd.build) and declares
+the C ABI of include/mla.h for ctypes.  There is no fallback: if the library
+is missing or does not load, importing the package fails with the reason."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+
+class Dims(ctypes.Structure):
+    """mla_dims_t (40 bytes)."""
+    _fields_ = [
+        ("n_heads", ctypes.c_int32),
+        ("d_c", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("d_nope", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("rope_base", ctypes.c_double),
+    ]
+
+
+assert ctypes.sizeof(Dims) == 40
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE = 3
+MLA_ERR_HIP = 4
+MLA_CACHE_BF16 = 0
+MLA_CACHE_FP8_E4M3 = 1
+MLA_APPEND_NO_ROPE = 1
+
+EXPORTS = (
+    "mla_append_latent", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_paged",
+    "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_profile_begin",
+    "mla_profile_end",
+)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_DP = ctypes.POINTER(Dims)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_nope_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.mla_append_latent.argtypes = [_DP, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
+                                      ctypes.c_uint32, _P]
+    lib.mla_append_latent.restype = ctypes.c_int
+    lib.mla_absorb_q.argtypes = [_DP, _P, _P, _P, _P, _I, _P, _P]
+    lib.mla_absorb_q.restype = ctypes.c_int
+    lib.mla_decode_workspace_size.argtypes = [_DP, _I, _I]
+    lib.mla_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mla_decode_paged.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, ctypes.c_size_t,
+                                     _P, _P, _P]
+    lib.mla_decode_paged.restype = ctypes.c_int
+    lib.mla_out_proj.argtypes = [_DP, _P, _P, _I, _P, _P]
+    lib.mla_out_proj.restype = ctypes.c_int
+    lib.mla_cache_bytes_per_token.argtypes = [_DP]
+    lib.mla_cache_bytes_per_token.restype = ctypes.c_size_t
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_profile_begin.argtypes = [_I]
+    lib.mla_profile_begin.restype = ctypes.c_int
+    lib.mla_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]
+    lib.mla_profile_end.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()

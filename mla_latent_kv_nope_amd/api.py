@@ -1,0 +1,197 @@
+"""Python binding of libmla: argument marshalling only.
+
+Each function checks tensor dtypes, shapes, devices and contiguity, then calls
+the C entry point of the same name with raw device pointers and torch's
+current HIP stream.  Every step of MLA decode runs in the library's kernels;
+PyTorch only provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _native
+from ._native import Dims, lib
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)}")
+
+
+def status_string(status: int) -> str:
+    return lib.mla_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != _native.MLA_OK:
+        raise MlaError(fn, status)
+
+
+def make_dims(n_heads: int, d_c: int, d_rope: int, d_nope: int, d_v: int, page_size: int,
+              fp8: bool = False, softmax_scale: Optional[float] = None,
+              rope_base: float = 10000.0) -> Dims:
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_nope + d_rope)
+    return Dims(n_heads, d_c, d_rope, d_nope, d_v, page_size,
+                _native.MLA_CACHE_FP8_E4M3 if fp8 else _native.MLA_CACHE_BF16,
+                float(softmax_scale), float(rope_base))
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _req(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Optional[tuple] = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _is_fp8(d: Dims) -> bool:
+    return d.cache_dtype == _native.MLA_CACHE_FP8_E4M3
+
+
+def pool_shape(d: Dims, num_pages: int) -> tuple:
+    return (num_pages, d.page_size, d.d_c + d.d_rope)
+
+
+def new_pool(d: Dims, num_pages: int, device="cuda") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Allocate an (uninitialised) cache pool and, for fp8, its scale array."""
+    if _is_fp8(d):
+        return (torch.empty(pool_shape(d, num_pages), dtype=torch.uint8, device=device),
+                torch.empty((num_pages, d.page_size), dtype=torch.float32, device=device))
+    return torch.empty(pool_shape(d, num_pages), dtype=torch.bfloat16, device=device), None
+
+
+def append_latent(d: Dims, c_kv: torch.Tensor, k_pe: torch.Tensor, positions: torch.Tensor,
+                  seq_ids: torch.Tensor, block_table: torch.Tensor, pool: torch.Tensor,
+                  scales: Optional[torch.Tensor] = None, rope: bool = True) -> None:
+    T = c_kv.shape[0]
+    _req(c_kv, "c_kv", torch.bfloat16, (T, d.d_c))
+    _req(k_pe, "k_pe", torch.bfloat16, (T, d.d_rope))
+    _req(positions, "positions", torch.int32, (T,))
+    _req(seq_ids, "seq_ids", torch.int32, (T,))
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs][max_pages]")
+    _req(block_table, "block_table", torch.int32)
+    num_pages = pool.shape[0]
+    if _is_fp8(d):
+        _req(pool, "pool", torch.uint8, pool_shape(d, num_pages))
+        if scales is None:
+            raise ValueError("an fp8 cache needs its scales tensor")
+        _req(scales, "scales", torch.float32, (num_pages, d.page_size))
+    else:
+        _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+        if scales is not None:
+            raise ValueError("a bf16 cache has no scales")
+    st = lib.mla_append_latent(
+        ctypes.byref(d), _ptr(c_kv), _ptr(k_pe), _ptr(positions), _ptr(seq_ids), _ptr(block_table),
+        block_table.shape[0], block_table.shape[1], num_pages, T, _ptr(pool), _ptr(scales),
+        0 if rope else _native.MLA_APPEND_NO_ROPE, _stream())
+    _check("mla_append_latent", st)
+
+
+def absorb_q(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_pos: torch.Tensor,
+             w_uk: torch.Tensor, q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    B = q_nope.shape[0]
+    H = d.n_heads
+    _req(q_nope, "q_nope", torch.bfloat16, (B, H, d.d_nope))
+    _req(q_pe, "q_pe", torch.bfloat16, (B, H, d.d_rope))
+    _req(q_pos, "q_pos", torch.int32, (B,))
+    _req(w_uk, "w_uk", torch.bfloat16, (H, d.d_c, d.d_nope))
+    if q_out is None:
+        q_out = torch.empty((B, H, d.d_c + d.d_rope), dtype=torch.bfloat16, device=q_nope.device)
+    _req(q_out, "q_out", torch.bfloat16, (B, H, d.d_c + d.d_rope))
+    _check("mla_absorb_q", lib.mla_absorb_q(ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(q_pos),
+                                            _ptr(w_uk), B, _ptr(q_out), _stream()))
+    return q_out
+
+
+def decode_workspace_size(d: Dims, B: int, num_splits: int = 0) -> int:
+    n = lib.mla_decode_workspace_size(ctypes.byref(d), int(B), int(num_splits))
+    if n == 0:
+        raise MlaError("mla_decode_workspace_size", _native.MLA_ERR_UNSUPPORTED)
+    return int(n)
+
+
+def new_workspace(d: Dims, B: int, num_splits: int = 0, device="cuda") -> torch.Tensor:
+    return torch.empty(decode_workspace_size(d, B, num_splits), dtype=torch.uint8, device=device)
+
+
+def decode_paged(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Optional[torch.Tensor],
+                 block_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int = 0,
+                 workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    B = q.shape[0]
+    H, R = d.n_heads, d.d_c + d.d_rope
+    _req(q, "q", torch.bfloat16, (B, H, R))
+    num_pages = pool.shape[0]
+    if _is_fp8(d):
+        _req(pool, "pool", torch.uint8, pool_shape(d, num_pages))
+        _req(scales, "scales", torch.float32, (num_pages, d.page_size))
+    else:
+        _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages]")
+    _req(block_table, "block_table", torch.int32)
+    _req(seq_lens, "seq_lens", torch.int32, (B,))
+    if workspace is None:
+        workspace = new_workspace(d, B, num_splits, q.device)
+    _req(workspace, "workspace", torch.uint8)
+    if o_lat is None:
+        o_lat = torch.empty((B, H, d.d_c), dtype=torch.bfloat16, device=q.device)
+    _req(o_lat, "o_lat", torch.bfloat16, (B, H, d.d_c))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _req(lse, "lse", torch.float32, (B, H))
+    st = lib.mla_decode_paged(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales), _ptr(block_table),
+                              block_table.shape[1], num_pages, _ptr(seq_lens), B, int(num_splits),
+                              _ptr(workspace), workspace.numel(), _ptr(o_lat), _ptr(lse), _stream())
+    _check("mla_decode_paged", st)
+    return o_lat, lse
+
+
+def out_proj(d: Dims, o_lat: torch.Tensor, w_uv: torch.Tensor,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    B = o_lat.shape[0]
+    H = d.n_heads
+    _req(o_lat, "o_lat", torch.bfloat16, (B, H, d.d_c))
+    _req(w_uv, "w_uv", torch.bfloat16, (H, d.d_c, d.d_v))
+    if out is None:
+        out = torch.empty((B, H, d.d_v), dtype=torch.bfloat16, device=o_lat.device)
+    _req(out, "out", torch.bfloat16, (B, H, d.d_v))
+    _check("mla_out_proj", lib.mla_out_proj(ctypes.byref(d), _ptr(o_lat), _ptr(w_uv), B, _ptr(out),
+                                            _stream()))
+    return out
+
+
+def cache_bytes_per_token(d: Dims) -> int:
+    return int(lib.mla_cache_bytes_per_token(ctypes.byref(d)))
+
+
+def profile_begin(max_records: int) -> None:
+    _check("mla_profile_begin", lib.mla_profile_begin(int(max_records)))
+
+
+def profile_end() -> Tuple[float, int]:
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    _check("mla_profile_end", lib.mla_profile_end(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,551 @@
+// mla_decode_paged: single-query softmax attention of all heads over the paged
+// latent cache, with the latent used as V (absorbed MLA decode).
+//
+// Method: "DeepSeek-V2拆解：MLA与MoE如何把KV缓存压降93.3%" (sheratonhq.com)
+// section 2.1 (cache only the latent; absorb W_UK / W_UV) and
+// "LLM推理优化的新范式：从内存墙到计算墙的跨越" (zskr.cn) section 2.2 (the
+// reordered path scores Q.W_UK directly against the compressed cache).  The
+// split into partial results merged by their log-sum-exp is this library's
+// own design; the pages do not describe one.
+//
+// Three kernels, all enqueued on the caller's stream:
+//   k_plan    one workgroup: tiles per sequence (32 tokens each), their prefix
+//             sums, and the per-workgroup quota = ceil(total tiles / parts).
+//   k_split   workgroup w takes global tiles [w*quota, (w+1)*quota) of the
+//             concatenated batch; a range may cover the tail of one sequence
+//             and the head of the next.  For every (w, b) piece it streams the
+//             tiles and writes either the final o_lat/lse (the piece is the
+//             whole sequence) or a normalised partial O and its lse to slot
+//             w + b of the workspace.
+//   k_combine merges the partial pieces of every split sequence.
+//
+// k_split design (gfx950): a workgroup of NW waves x 16 heads works on one
+// (sequence piece, head group); with NW = 8 one workgroup holds all 128 heads, so
+// each 32-token tile of 576-element rows is fetched from HBM once and shared by
+// every head.  Tiles are gathered page by page with direct global->LDS 16-byte
+// loads into a ring of NBUF buffers (the next NBUF-1 tiles are in flight while
+// one is consumed); 16-byte chunks are XOR-swizzled within groups of 8 so that
+// the row-strided MFMA operand reads spread over the LDS banks.  Per tile and wave:
+//   S^T (2 x 16 tokens x 16 heads) = K_tile . Q^T   on 16x16x32 bf16 MFMA (K_tile
+//        rows are the A operand straight from LDS; Q stays in 72 VGPRs),
+//   online softmax in the base-2 domain; the row max is shared by the four
+//        lanes holding a head (permlane16 + permlane32 swaps); lazy rescale:
+//        the exponent offset only moves when a new maximum exceeds it by more
+//        than 8 (so P <= 2^8),
+//   O (16 heads x d_c) += P . V_tile                  on 16x16x32 bf16 MFMA; P
+//        leaves the S^T accumulator already in A-operand order and V_tile is
+//        read with the LDS transpose read.  O lives in 128 accumulator registers.
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+
+namespace mla {
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+// With the exponent offset fixed per piece, P = 2^(x - m) stays below
+// 2^kHeadroom (far inside fp32 and bf16 range) unless a score exceeds the
+// offset by more than that; such a piece is recomputed with its true maximum.
+constexpr float kHeadroom = 64.0f;  // log2 units
+
+template <int DC, int DR, int NW>
+struct DecodeCfg {
+  static constexpr int R = DC + DR;
+  static constexpr int ROWB = 2 * R;                 // bytes per bf16 row
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  // Blocked LDS layout (rows of a multiple of 8 chunks): the tile is a grid of
+  // 1 KB blocks of 8 rows x 8 chunks; inside a block, chunk c of row r sits at
+  // position r*8 + (c ^ r).  Otherwise plain row-major.
+  static constexpr bool BLOCKED = (CPR % 8) == 0;
+  static constexpr int CG = CPR / 8;                 // chunk groups per row (blocked)
+  static constexpr int TILE_BYTES = kTile * ROWB;
+  static constexpr int INSTR = kTile * CPR / 64;     // 1 KB wave loads per tile
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int LD_HI = (INSTR + NW - 1) / NW;  // loads of waves < INSTR % NW (or all)
+  static constexpr int LD_LO = INSTR / NW;
+  static constexpr int K32 = R / 32;                 // full 32-wide QK chunks
+  static constexpr bool K16 = (R % 32) == 16;        // one 16-wide tail chunk
+  static constexpr int VCB = DC / 16;                // PV column blocks
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int nbuf() {
+    int n = 2;
+    while ((n + 1) * TILE_BYTES <= LDS_MAX && (n - 1) * LD_HI <= 63 && n < 4) ++n;
+    return n;
+  }
+  static constexpr int NBUF = nbuf();
+  static_assert(R % 16 == 0 && DC % 16 == 0, "dims");
+  static_assert((kTile * CPR) % 64 == 0, "tile load split");
+  static_assert((NBUF - 2) * LD_HI <= 63, "vmcnt range");
+};
+
+// byte offset of (row t, 16-byte chunk c) inside a tile buffer
+template <class Cfg>
+__device__ __forceinline__ uint32_t lds_off(int t, int c) {
+  if constexpr (Cfg::BLOCKED)
+    return ((t >> 3) * Cfg::CG + (c >> 3)) * 1024 + (t & 7) * 128 + (((c & 7) ^ (t & 7)) * 16);
+  else
+    return t * Cfg::ROWB + c * 16;
+}
+
+// waits until at most `pending` tiles' loads of this wave (L loads per tile)
+// are outstanding
+template <int NBUF, int L>
+__device__ __forceinline__ void wait_tiles(int pending) {
+  if constexpr (NBUF >= 4) {
+    if (pending >= 2) { wait_vmcnt<2 * L>(); return; }
+  }
+  if constexpr (NBUF >= 3) {
+    if (pending >= 1) { wait_vmcnt<L>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Scheduling hint for a run of N MFMAs, each fed by RD LDS reads: issue the
+// reads of the first AHEAD MFMAs, then alternate one MFMA with the reads of
+// the MFMA AHEAD places later.  Bounds the registers held by in-flight reads.
+template <int N, int RD, int AHEAD_MAX>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int AHEAD = AHEAD_MAX < N ? AHEAD_MAX : N - 1;
+  static_assert(AHEAD >= 1, "run too short");
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+__device__ __forceinline__ int clamp_len(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* seq_lens, int B, int cap,
+                                               int num_parts, int32_t* plan) {
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 1024) {
+    const int b = base + threadIdx.x;
+    const int n = b < B ? (clamp_len(seq_lens[b], cap) + kTile - 1) / kTile : 0;
+    scan[threadIdx.x] = n;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (b < B) plan[b] = carry + scan[threadIdx.x] - n;  // exclusive prefix
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += scan[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int total = carry;
+    plan[B] = total;
+    plan[B + 1] = total > 0 ? (total + num_parts - 1) / num_parts : 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int DC, int DR, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu((NW + 3) / 4, (NW + 3) / 4)))
+void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
+             const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table) {
+  using Cfg = DecodeCfg<DC, DR, NW>;
+  constexpr int R = Cfg::R, ROWB = Cfg::ROWB, CPR = Cfg::CPR;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES];
+  __shared__ int redo;
+
+  // workgroup -> (part, head group); the head groups of one part are 8 ids apart,
+  // which places them on the same XCD (ids are dealt round-robin to the 8 XCDs)
+  // so the second reader of a tile finds it in that XCD's L2.
+  const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
+  const int hg = y % head_groups;
+  const int w = (y / head_groups) * 8 + xcd;
+
+  // plan, seq_lens and block_table are read with scalar loads (restrict lets
+  // the compiler prove nothing here writes them); scalar loads wait on their
+  // own counter, so they never force a wait for the in-flight tile loads.
+  const int B = a.B, H = a.H;
+  const int total = plan[B];
+  const int quota = plan[B + 1];
+  int g = w * quota;
+  const int gend = min(g + quota, total);
+  if (g >= gend) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int quad = lane >> 4;          // k slice (operands) / token quad (S) / head quad (O)
+  const int l16 = lane & 15;
+  const int lg = a.page_size_log2;
+  const int ps = 1 << lg;
+  const int cap = a.max_pages << lg;
+  const int hbase = (hg * NW + wave) * 16;   // first head of this wave
+  constexpr int REM = Cfg::INSTR % NW;
+  const bool hi_loader = REM == 0 || wave < REM;
+
+  // rows that are skipped keep whatever the buffer held; start from zeros so it is finite
+  for (int i = threadIdx.x; i < Cfg::NBUF * Cfg::TILE_BYTES / 16; i += Cfg::THREADS)
+    reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  // first sequence of this range: the largest b with plan[b] <= g
+  int b;
+  {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (plan[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+
+  // Per-lane LDS byte offsets (relative to a tile buffer) of the MFMA operand
+  // reads; every other operand address is one of these plus an immediate.
+  // QK: row l16 (+16 per token block), chunk 4kc + quad: an even/odd base plus
+  // 1 KB per chunk group (blocked) or 64 bytes per kc (row-major).
+  const uint32_t qk_even = lds_off<Cfg>(l16, quad);
+  const uint32_t qk_odd = lds_off<Cfg>(l16, 4 + quad);
+  // QK tail (16-wide chunk, row-major layouts only): elements 32*K32 + 4*quad .. +4
+  const uint32_t qk_tail = lds_off<Cfg>(l16, (32 * Cfg::K32 + 4 * quad) >> 3) +
+                           ((32 * Cfg::K32 + 4 * quad) & 7) * 2;
+  // PV transpose reads: source lane 4r+q of its group reads row 4*quad + r (+16),
+  // chunk 2cb + q/2, bytes 8*(q%2): one of four bases (cb % 4) plus 1 KB per cb/4
+  // (blocked), or one base plus 32 bytes per cb (row-major).
+  uint32_t pv_base[4];
+  {
+    const int trr = l16 >> 2, trq = l16 & 3;
+    const int trow = 4 * quad + trr;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pv_base[m] = lds_off<Cfg>(trow, 2 * m + (trq >> 1)) + (trq & 1) * 8;
+  }
+  // Tile loads (blocked): lane l of every 1 KB load fills row l/8 of its block
+  // with logical chunk (l%8) ^ (l/8); the per-lane source offset is the same for
+  // every block.
+  const int ld_r = lane >> 3;
+  const uint32_t ld_off = ld_r * ROWB + (((lane & 7) ^ ld_r) * 16);
+  const uint32_t ld_fb = ((lane & 7) ^ ld_r) * 16;   // same chunk of the block's first row
+
+  while (g < gend) {
+    const int t0 = plan[b], t1 = plan[b + 1];
+    const int lt0 = g - t0, lt1 = min(gend, t1) - t0;
+    const int ntiles = lt1 - lt0;
+    const int S = clamp_len(seq_lens[b], cap);
+    const bool whole = (lt0 == 0) && (lt1 == t1 - t0);
+    const int32_t* bt = block_table + static_cast<int64_t>(b) * a.max_pages;
+    const char* pool = static_cast<const char*>(a.pool);
+    const int64_t page_bytes = static_cast<int64_t>(ROWB) << lg;
+
+    // Rows past the sequence (or on a page id outside the pool) load the same
+    // chunk of the tile's first row instead, which is always a valid token.
+    auto page_base = [&](int tok) -> const char* {
+      const int pg = bt[tok >> lg];
+      return (pg >= 0 && pg < a.num_pages) ? pool + pg * page_bytes + (tok & (ps - 1)) * ROWB
+                                           : nullptr;
+    };
+    auto issue_tile = [&](int lt, int buf) {
+      const int tok0 = lt * kTile;
+      const char* row0 = page_base(tok0);
+      const char* fb = row0 ? row0 : pool;
+      char* dst_tile = lds + buf * Cfg::TILE_BYTES;
+#pragma unroll
+      for (int k = 0; k < Cfg::LD_HI; ++k) {
+        const int blk = k * NW + wave;               // 1 KB block of the tile this load fills
+        if (blk < Cfg::INSTR) {
+          const char* src;
+          if constexpr (Cfg::BLOCKED) {
+            const int bi = blk / Cfg::CG, bj = blk - bi * Cfg::CG;
+            const int rtok = tok0 + 8 * bi;          // first token of the block's 8 rows
+            const char* rb = (ps >= kTile || bi < 2) ? row0 + 8 * bi * ROWB : page_base(rtok);
+            const bool ok = rb != nullptr && row0 != nullptr && rtok + ld_r < S;
+            src = ok ? rb + bj * 128 + ld_off : fb + bj * 128 + ld_fb;
+          } else {
+            const int pos = blk * 64 + lane;         // chunk position in the row-major tile
+            const int t = pos / CPR;
+            const int c = pos - t * CPR;
+            const char* rb = (ps >= kTile || t < 16) ? row0 : page_base(tok0 + 16);
+            const bool ok = rb != nullptr && row0 != nullptr && tok0 + t < S;
+            src = ok ? rb + ((ps >= kTile || t < 16) ? t : t - 16) * ROWB + c * 16 : fb + c * 16;
+          }
+          __builtin_amdgcn_global_load_lds(
+              reinterpret_cast<const void*>(src),
+              reinterpret_cast<lds_void_t*>(reinterpret_cast<uintptr_t>(dst_tile + blk * 1024)),
+              16, 0, 0);
+        }
+      }
+    };
+
+    // query registers: lane holds head hbase + l16, elements [32kc + 8*quad, +8)
+    bf16x8 qreg[Cfg::K32];
+    bf16x4 qtail = {};
+    {
+      const int h = hbase + l16;
+      const bool hv = h < H;
+      const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * H + (hv ? h : 0)) * R;
+      const bf16x8 z = {};
+#pragma unroll
+      for (int kc = 0; kc < Cfg::K32; ++kc) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * kc + 8 * quad);
+        qreg[kc] = hv ? v : z;
+      }
+      if constexpr (Cfg::K16) {
+        const bf16x4 v = *reinterpret_cast<const bf16x4*>(qrow + 32 * Cfg::K32 + 4 * quad);
+        const bf16x4 z4 = {};
+        qtail = hv ? v : z4;
+      }
+    }
+
+    f32x4 o[Cfg::VCB];
+    float m_use = -INFINITY;   // exponent offset for this lane's head (set by the first tile)
+    float m_seen = -INFINITY;  // running maximum of this head's scores
+    float l_part = 0.f;        // this lane's share of the softmax denominator
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < Cfg::VCB; ++cb) o[cb] = f32x4{};
+    l_part = 0.f;
+    bool overflow = false;
+
+    // prologue: put the first NBUF-1 tiles in flight
+#pragma unroll
+    for (int i = 0; i < Cfg::NBUF - 1; ++i)
+      if (i < ntiles) issue_tile(lt0 + i, i);
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int pending = min(ntiles - 1 - it, Cfg::NBUF - 2);
+      if (hi_loader) wait_tiles<Cfg::NBUF, Cfg::LD_HI>(pending);
+      else wait_tiles<Cfg::NBUF, Cfg::LD_LO>(pending);
+      block_barrier();
+      if (it + Cfg::NBUF - 1 < ntiles)
+        issue_tile(lt0 + it + Cfg::NBUF - 1, (it + Cfg::NBUF - 1) % Cfg::NBUF);
+
+      const char* tb = lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES;
+      const int tok0 = (lt0 + it) * kTile;
+
+      // ---- S^T = K_tile . Q^T; token block tb: A operand = row 16tb + l16,
+      // 16-byte chunk 4kc + quad.  Rows l16 and 16 + l16 swizzle alike, and the
+      // swizzled chunk of kc is an even/odd base plus 8*(kc/2) chunks.
+      f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int tbk = 0; tbk < 2; ++tbk) {
+#pragma unroll
+        for (int kc = 0; kc < Cfg::K32; ++kc) {
+          const char* ap = tb + ((kc & 1) ? qk_odd : qk_even) + tbk * 16 * ROWB +
+                           (Cfg::BLOCKED ? 1024 * (kc >> 1) : 64 * (kc & ~1));
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(ap);
+          sacc[tbk] = mfma16(av, qreg[kc], sacc[tbk]);
+        }
+        if constexpr (Cfg::K16) {
+          const bf16x4 av = *reinterpret_cast<const bf16x4*>(tb + qk_tail + tbk * 16 * ROWB);
+          sacc[tbk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, qtail), sacc[tbk], 0, 0, 0);
+        }
+      }
+      sched_interleave<2 * Cfg::K32 + (Cfg::K16 ? 2 : 0), 1, 3>();
+
+      // ---- online softmax; sacc[tb][i] is token 16tb + 4*quad + i, head l16
+      float x[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int tbk = 0; tbk < 2; ++tbk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * tbk + 4 * quad + i;
+          const float v = (tok0 + t < S) ? sacc[tbk][i] * a.scale_log2 : -INFINITY;
+          x[4 * tbk + i] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = max_across_half_waves(max_across_quarter_pairs(mt));
+      m_seen = fmaxf(m_seen, mt);
+      if (pass == 0 && it == 0) m_use = mt;       // first tile sets the offset; O is still zero
+      overflow |= mt > m_use + kHeadroom;
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = exp2f(x[j] - m_use);
+        l_part += p[j];
+      }
+      // PV A operand: k slot 8*quad + j <-> token (j < 4 ? 4quad + j : 16 + 4quad + j - 4)
+      uint32_t pu[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pu[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, pu);
+
+      // ---- O += P . V_tile.  Transpose-read source lane 4r+q of group `quad`
+      // reads token rows 4*quad + r and 16 + 4*quad + r at channels 16cb + 4q;
+      // the swizzled address is one of four bases (by cb % 4) plus immediates.
+#pragma unroll
+      for (int cb = 0; cb < Cfg::VCB; ++cb) {
+        const int imm = Cfg::BLOCKED ? 1024 * (cb >> 2) : 32 * cb;
+        const char* p0 = tb + (Cfg::BLOCKED ? pv_base[cb & 3] : pv_base[0]) + imm;
+        const bf16x4 v0 = lds_read_tr16(p0);
+        const bf16x4 v1 = lds_read_tr16(p0 + 16 * ROWB);
+        const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[cb] = mfma16(pa, bv, o[cb]);
+      }
+      sched_interleave<Cfg::VCB, 2, 2>();
+    }
+
+    // a score far above the offset anywhere in the workgroup: redo the piece
+    // with each head's true maximum as its offset (cannot overflow again)
+    if (threadIdx.x == 0) redo = 0;
+    __syncthreads();
+    if (__builtin_amdgcn_ballot_w64(overflow) != 0 && lane == 0) redo = 1;
+    __syncthreads();
+    const bool again = redo != 0;
+    __syncthreads();
+    if (!again) break;
+    m_use = m_seen;
+    }  // pass
+
+    // ---- epilogue: normalise and write
+    const float l_tot = sum_across_half_waves(sum_across_quarter_pairs(l_part));
+    const float inv = 1.0f / l_tot;
+    const float lse_nat = (m_use + log2f(l_tot)) * kLn2;
+    if (whole) {
+      uint16_t* ob = a.o_lat + static_cast<int64_t>(b) * H * DC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = shfl_f32(inv, 4 * quad + i);
+        const int h = hbase + 4 * quad + i;
+        if (h < H) {
+#pragma unroll
+          for (int cb = 0; cb < Cfg::VCB; ++cb)
+            ob[static_cast<int64_t>(h) * DC + 16 * cb + l16] = f32_to_bf16_bits(o[cb][i] * sc);
+        }
+      }
+      if (a.lse != nullptr && quad == 0 && hbase + l16 < H)
+        a.lse[static_cast<int64_t>(b) * H + hbase + l16] = lse_nat;
+    } else {
+      const int64_t slot = static_cast<int64_t>(w) + b;
+      float* po = a.part_o + slot * H * DC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = shfl_f32(inv, 4 * quad + i);
+        const int h = hbase + 4 * quad + i;
+        if (h < H) {
+#pragma unroll
+          for (int cb = 0; cb < Cfg::VCB; ++cb)
+            po[static_cast<int64_t>(h) * DC + 16 * cb + l16] = o[cb][i] * sc;
+        }
+      }
+      if (quad == 0 && hbase + l16 < H) a.part_lse[slot * H + hbase + l16] = lse_nat;
+    }
+
+    // next piece: the next non-empty sequence
+    g = t0 + lt1;
+    ++b;
+    while (b < B && plan[b + 1] <= g) ++b;
+    // all waves must be done reading the ring before the next piece refills it
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per (b, h): merge the pieces of split sequences; write zeros and
+// -inf for empty sequences.  Pieces computed whole were written by k_split.
+__global__ __launch_bounds__(256) void k_combine(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int B = a.B, H = a.H, DC = a.d_c;
+  if (bh >= B * H) return;
+  const int b = bh / H, h = bh - b * H;
+  const int t0 = a.plan[b], t1 = a.plan[b + 1];
+  const int quota = a.plan[B + 1];
+  uint16_t* ob = a.o_lat + static_cast<int64_t>(bh) * DC;
+  if (t1 == t0) {
+    for (int c = lane; c < DC; c += 64) ob[c] = 0;
+    if (a.lse != nullptr && lane == 0) a.lse[bh] = -INFINITY;
+    return;
+  }
+  const int wf = t0 / quota, wl = (t1 - 1) / quota;
+  if (wf == wl) return;
+  float mx = -INFINITY;
+  for (int wv = wf; wv <= wl; ++wv) mx = fmaxf(mx, a.part_lse[(static_cast<int64_t>(wv) + b) * H + h]);
+  float sum = 0.f;
+  for (int wv = wf; wv <= wl; ++wv) sum += expf(a.part_lse[(static_cast<int64_t>(wv) + b) * H + h] - mx);
+  const float lse_all = mx + logf(sum);
+  for (int c = lane; c < DC; c += 64) {
+    float acc = 0.f;
+    for (int wv = wf; wv <= wl; ++wv) {
+      const int64_t slot = static_cast<int64_t>(wv) + b;
+      const float wgt = expf(a.part_lse[slot * H + h] - lse_all);
+      acc += wgt * a.part_o[(slot * H + h) * DC + c];
+    }
+    ob[c] = f32_to_bf16_bits(acc);
+  }
+  if (a.lse != nullptr && lane == 0) a.lse[bh] = lse_all;
+}
+
+template <int DC, int DR, int NW>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
+  const int hg = (a.H + 16 * NW - 1) / (16 * NW);
+  const int parts8 = (a.num_parts + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_split<DC, DR, NW>), dim3(parts8 * hg), dim3(64 * NW), 0, s, a, hg,
+                     static_cast<const int32_t*>(a.plan), a.seq_lens, a.block_table);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_supported(int d_c, int d_rope, int H) {
+  if (H < 1 || H > 128) return false;
+  if (d_c == 512 && d_rope == 64) return true;
+  if (d_c == 32 && d_rope == 16) return H <= 32;
+  return false;
+}
+
+int decode_auto_parts(int B, int H) {
+  (void)B;
+  (void)H;
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  WorkspaceLayout L;
+  L.plan_off = 0;
+  L.part_o_off = up(sizeof(int32_t) * (static_cast<size_t>(B) + 2));
+  const size_t slots = static_cast<size_t>(num_parts) + B;
+  L.part_lse_off = L.part_o_off + up(sizeof(float) * slots * H * d_c);
+  L.total = L.part_lse_off + up(sizeof(float) * slots * H);
+  return L;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, a.seq_lens, a.B, a.max_pages << a.page_size_log2,
+                     a.num_parts, a.plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+#ifndef MLA_DECODE_WAVES
+#define MLA_DECODE_WAVES 8
+#endif
+  if (a.d_c == 512 && a.d_rope == 64) {
+    if (a.H <= 16) e = launch_split<512, 64, 1>(a, s);
+    else if (a.H <= 32) e = launch_split<512, 64, 2>(a, s);
+    else e = launch_split<512, 64, MLA_DECODE_WAVES>(a, s);
+  } else if (a.d_c == 32 && a.d_rope == 16) {
+    if (a.H <= 16) e = launch_split<32, 16, 1>(a, s);
+    else e = launch_split<32, 16, 2>(a, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+  const int waves = a.B * a.H;
+  hipLaunchKernelGGL(k_combine, dim3((waves + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,260 @@
+// C ABI of libmla (declared in include/mla.h): argument validation, workspace
+// layout, dispatch to the kernels, status codes, and the optional kernel
+// timing hooks.  Every check here runs before any HIP call, so invalid host
+// arguments enqueue nothing.
+#include "../../include/mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <vector>
+
+#include "mla_internal.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+// Dimension checks shared by all calls.
+mla_status_t check_dims(const mla_dims_t* d) {
+  if (d == nullptr) return MLA_ERR_INVALID_ARG;
+  if (d->n_heads <= 0 || d->d_c <= 0 || d->d_rope <= 0 || d->d_nope <= 0 || d->d_v <= 0 ||
+      d->page_size <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (d->d_rope % 2 != 0) return MLA_ERR_INVALID_ARG;
+  if (d->cache_dtype != MLA_CACHE_BF16 && d->cache_dtype != MLA_CACHE_FP8_E4M3)
+    return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(d->rope_base) || d->rope_base <= 0.0) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(d->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  const bool v3 = d->d_c == 512 && d->d_rope == 64 && d->d_nope == 128 && d->d_v == 128;
+  const bool tiny = d->d_c == 32 && d->d_rope == 16 && d->d_nope == 16 && d->d_v == 16;
+  if (!v3 && !tiny) return MLA_ERR_UNSUPPORTED;
+  if (d->n_heads > (tiny ? 32 : 128)) return MLA_ERR_UNSUPPORTED;
+  const int lg = log2_exact(d->page_size);
+  if (lg < 4 || lg > 8) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+struct Profiler {
+  bool active = false;
+  std::vector<hipEvent_t> ev;  // [2 * max_records]: start, stop pairs
+  int used = 0;
+};
+Profiler g_prof;
+
+int effective_parts(int32_t num_splits, int B, int H) {
+  return num_splits > 0 ? num_splits : mla::decode_auto_parts(B, H);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+size_t mla_cache_bytes_per_token(const mla_dims_t* d) {
+  if (d == nullptr || d->d_c <= 0 || d->d_rope < 0) return 0;
+  const size_t r = static_cast<size_t>(d->d_c) + static_cast<size_t>(d->d_rope);
+  if (d->cache_dtype == MLA_CACHE_BF16) return 2 * r;
+  if (d->cache_dtype == MLA_CACHE_FP8_E4M3) return r + 4;
+  return 0;
+}
+
+mla_status_t mla_append_latent(const mla_dims_t* d, const void* c_kv, const void* k_pe,
+                               const int32_t* positions, const int32_t* seq_ids,
+                               const int32_t* block_table, int32_t num_seqs, int32_t max_pages,
+                               int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
+                               uint32_t flags, void* stream) {
+  const mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0 || num_seqs <= 0 || max_pages <= 0 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
+  if ((flags & ~MLA_APPEND_NO_ROPE) != 0) return MLA_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MLA_OK;
+  if (!c_kv || !k_pe || !positions || !seq_ids || !block_table || !pool) return MLA_ERR_INVALID_ARG;
+  const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
+  if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(c_kv, 16) || !aligned(k_pe, 4) || !aligned(pool, 16) || !aligned(positions, 4) ||
+      !aligned(seq_ids, 4) || !aligned(block_table, 4) || (fp8 && !aligned(scales, 4)))
+    return MLA_ERR_INVALID_ARG;
+  mla::AppendArgs a{};
+  a.d_c = d->d_c;
+  a.d_rope = d->d_rope;
+  a.page_size_log2 = log2_exact(d->page_size);
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.num_seqs = num_seqs;
+  a.n_tokens = n_tokens;
+  a.fp8 = fp8;
+  a.rope = (flags & MLA_APPEND_NO_ROPE) == 0;
+  a.rope_base = d->rope_base;
+  a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.positions = positions;
+  a.seq_ids = seq_ids;
+  a.block_table = block_table;
+  a.pool = pool;
+  a.scales = scales;
+  return from_hip(mla::launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_absorb_q(const mla_dims_t* d, const void* q_nope, const void* q_pe,
+                          const int32_t* q_pos, const void* w_uk, int32_t B, void* q_out,
+                          void* stream) {
+  const mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (B <= 0) return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !q_pe || !q_pos || !w_uk || !q_out) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 4) || !aligned(q_pos, 4) || !aligned(w_uk, 16) ||
+      !aligned(q_out, 16))
+    return MLA_ERR_INVALID_ARG;
+  if (!mla::absorb_supported(d->d_c, d->d_nope)) return MLA_ERR_UNSUPPORTED;
+  mla::AbsorbArgs a{};
+  a.B = B;
+  a.H = d->n_heads;
+  a.d_c = d->d_c;
+  a.d_rope = d->d_rope;
+  a.d_nope = d->d_nope;
+  a.rope_base = d->rope_base;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.q_pos = q_pos;
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.q_out = static_cast<uint16_t*>(q_out);
+  return from_hip(mla::launch_absorb(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_decode_workspace_size(const mla_dims_t* d, int32_t B, int32_t num_splits) {
+  if (check_dims(d) != MLA_OK || B <= 0 || num_splits < 0) return 0;
+  if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads)) return 0;
+  const int parts = effective_parts(num_splits, B, d->n_heads);
+  return mla::decode_workspace_layout(B, d->n_heads, d->d_c, parts).total;
+}
+
+mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* pool,
+                              const float* scales, const int32_t* block_table, int32_t max_pages,
+                              int32_t num_pages, const int32_t* seq_lens, int32_t B,
+                              int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
+                              float* lse, void* stream) {
+  const mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (B <= 0 || max_pages <= 0 || num_pages <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
+  if (!q || !pool || !block_table || !seq_lens || !workspace || !o_lat) return MLA_ERR_INVALID_ARG;
+  const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
+  if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(workspace, 256) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)) ||
+      (fp8 && !aligned(scales, 16)))
+    return MLA_ERR_INVALID_ARG;
+  if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads)) return MLA_ERR_UNSUPPORTED;
+  if (fp8) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_UNSUPPORTED;
+  const int parts = effective_parts(num_splits, B, d->n_heads);
+  const mla::WorkspaceLayout L = mla::decode_workspace_layout(B, d->n_heads, d->d_c, parts);
+  if (ws_bytes < L.total) return MLA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  mla::DecodeArgs a{};
+  a.B = B;
+  a.H = d->n_heads;
+  a.d_c = d->d_c;
+  a.d_rope = d->d_rope;
+  a.page_size_log2 = log2_exact(d->page_size);
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.num_parts = parts;
+  a.fp8 = fp8;
+  a.scale_log2 = static_cast<float>(static_cast<double>(d->softmax_scale) * 1.4426950408889634);
+  a.q = static_cast<const uint16_t*>(q);
+  a.pool = pool;
+  a.scales = scales;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
+  a.part_o = reinterpret_cast<float*>(ws + L.part_o_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.part_lse_off);
+  a.o_lat = static_cast<uint16_t*>(o_lat);
+  a.lse = lse;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_prof.active && 2 * g_prof.used + 1 < static_cast<int>(g_prof.ev.size())) {
+    e0 = g_prof.ev[2 * g_prof.used];
+    e1 = g_prof.ev[2 * g_prof.used + 1];
+    ++g_prof.used;
+  }
+  return from_hip(mla::launch_decode(a, static_cast<hipStream_t>(stream), e0, e1));
+}
+
+mla_status_t mla_out_proj(const mla_dims_t* d, const void* o_lat, const void* w_uv, int32_t B,
+                          void* out, void* stream) {
+  const mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (B <= 0) return MLA_ERR_INVALID_ARG;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned(o_lat, 16) || !aligned(w_uv, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARG;
+  if (!mla::out_proj_supported(d->d_c, d->d_v)) return MLA_ERR_UNSUPPORTED;
+  mla::OutProjArgs a{};
+  a.B = B;
+  a.H = d->n_heads;
+  a.d_c = d->d_c;
+  a.d_v = d->d_v;
+  a.o_lat = static_cast<const uint16_t*>(o_lat);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.out = static_cast<uint16_t*>(out);
+  return from_hip(mla::launch_out_proj(a, static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_profile_begin(int32_t max_records) {
+  if (max_records <= 0 || g_prof.active) return MLA_ERR_INVALID_ARG;
+  g_prof.ev.assign(2 * static_cast<size_t>(max_records), nullptr);
+  for (auto& e : g_prof.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto& x : g_prof.ev)
+        if (x) (void)hipEventDestroy(x);
+      g_prof.ev.clear();
+      return MLA_ERR_HIP;
+    }
+  }
+  g_prof.used = 0;
+  g_prof.active = true;
+  return MLA_OK;
+}
+
+mla_status_t mla_profile_end(double* total_ms, int32_t* n_records) {
+  if (!g_prof.active) return MLA_ERR_INVALID_ARG;
+  mla_status_t st = MLA_OK;
+  double sum = 0.0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) { st = MLA_ERR_HIP; break; }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) {
+      st = MLA_ERR_HIP;
+      break;
+    }
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (n_records) *n_records = g_prof.used;
+  for (auto& e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.used = 0;
+  g_prof.active = false;
+  return st;
+}
+
+}  // extern "C"

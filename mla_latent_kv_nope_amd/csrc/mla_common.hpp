@@ -1,0 +1,100 @@
+// Device-side helpers shared by the libmla kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kWave = 64;
+
+// ---- bf16 <-> fp32 --------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite and infinite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (the compiler emits the
+// gfx950 packed conversion for this pattern).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- MFMA wrappers (layouts verified on gfx950) ---------------------------
+// 32x32x16 bf16: A lane l holds row l%32, k = 8*(l/32)+[0,8); B lane l holds
+// column l%32, same k; C element i of lane l is C[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x32 bf16: A lane l holds row l%16, k = 8*(l/16)+[0,8); B lane l holds
+// column l%16, same k; C element i of lane l is C[4*(l/16) + i][l%16].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- LDS transpose read ---------------------------------------------------
+// Within each group of 16 lanes, destination lane i receives element (i%4) of
+// the 8 bytes read by source lane 4*e + i/4, for e = 0..3.  With source lane
+// 4r+q pointing at row r, columns [4q, 4q+4) of a row-major 16-bit tile, lane i
+// receives column i of rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds_ptr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(lds_ptr)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// ---- waits and barriers ---------------------------------------------------
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that also stops the compiler moving memory operations across it.
+__device__ __forceinline__ void block_barrier() {
+  __asm__ __volatile__("s_barrier" ::: "memory");
+}
+
+// ---- cross-lane helpers ---------------------------------------------------
+__device__ __forceinline__ float max_across_half_waves(float x) {
+  // {x[l], x[l ^ 32]} as a pair on every lane
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_half_waves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// {x[l], x[l ^ 16]} as a pair on every lane
+__device__ __forceinline__ float max_across_quarter_pairs(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_quarter_pairs(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float shfl_f32(float x, int src_lane) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+}  // namespace mla

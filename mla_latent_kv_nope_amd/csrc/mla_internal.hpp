@@ -1,0 +1,87 @@
+// Internal launch interface between the C ABI layer (mla_api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Tokens per decode tile; the split plan and the decode kernel cut work in
+// whole tiles.
+constexpr int kTile = 32;
+
+// Heads handled by one wave of the decode kernel (16x16 MFMA columns).
+constexpr int kHeadsPerWave = 16;
+
+struct AppendArgs {
+  int d_c, d_rope, page_size_log2, max_pages, num_pages, num_seqs, n_tokens;
+  bool fp8, rope;
+  double rope_base;
+  const uint16_t* c_kv;
+  const uint16_t* k_pe;
+  const int32_t* positions;
+  const int32_t* seq_ids;
+  const int32_t* block_table;
+  void* pool;
+  float* scales;
+};
+
+struct AbsorbArgs {
+  int B, H, d_c, d_rope, d_nope;
+  double rope_base;
+  const uint16_t* q_nope;
+  const uint16_t* q_pe;
+  const int32_t* q_pos;
+  const uint16_t* w_uk;
+  uint16_t* q_out;
+};
+
+struct OutProjArgs {
+  int B, H, d_c, d_v;
+  const uint16_t* o_lat;
+  const uint16_t* w_uv;
+  uint16_t* out;
+};
+
+// Workspace of mla_decode_paged, carved from the caller's buffer:
+//   plan      int32 [B + 1] tile prefix sums, then int32 quota, total
+//   part_o    fp32 [num_parts + B][H][d_c]  normalised partial outputs
+//   part_lse  fp32 [num_parts + B][H]
+// A partial computed by workgroup w for sequence b lives in slot w + b.
+struct DecodeArgs {
+  int B, H, d_c, d_rope, page_size_log2, max_pages, num_pages, num_parts;
+  bool fp8;
+  float scale_log2;  // softmax_scale * log2(e)
+  const uint16_t* q;
+  const void* pool;
+  const float* scales;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t* plan;
+  float* part_o;
+  float* part_lse;
+  uint16_t* o_lat;
+  float* lse;
+};
+
+struct WorkspaceLayout {
+  size_t plan_off, part_o_off, part_lse_off, total;
+};
+
+WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts);
+int decode_auto_parts(int B, int H);
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s);
+hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t s);
+// plan + split kernel + combine; `ev0`/`ev1` (may be null) are recorded
+// immediately before and after the split kernel.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+bool decode_supported(int d_c, int d_rope, int H);
+bool absorb_supported(int d_c, int d_nope);
+bool out_proj_supported(int d_c, int d_v);
+
+}  // namespace mla

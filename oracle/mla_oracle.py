@@ -104,6 +104,16 @@ def fp8_quantize_rows(rows_f32: np.ndarray):
     return codes, scale
 
 
+def fp8_cache_codes(c_kv_bits: np.ndarray, k_pe_bits: np.ndarray, positions: np.ndarray,
+                    base: float):
+    """The fp8 cache content of a run of tokens: the row (c_kv || RoPE(k_pe))
+    rounded to fp32, then `fp8_quantize_rows`.  Returns (codes [T][R], scale [T])."""
+    C = bf16_bits_to_f64(c_kv_bits)
+    Kr = rope(bf16_bits_to_f64(k_pe_bits), positions, base)
+    row = np.concatenate([C, Kr], axis=-1).astype(np.float32)
+    return fp8_quantize_rows(row)
+
+
 def cache_rows(c_kv_bits: np.ndarray, k_pe_bits: np.ndarray, positions: np.ndarray,
                base: float, fp8: bool):
     """Mathematical content of the cached rows for a run of tokens.
@@ -113,15 +123,14 @@ def cache_rows(c_kv_bits: np.ndarray, k_pe_bits: np.ndarray, positions: np.ndarr
     RoPE part rotated at its own position.  For an fp8 cache the row (C || Kr)
     is first rounded to fp32, encoded as above and decoded back (code * scale).
     """
+    if fp8:
+        codes, scale = fp8_cache_codes(c_kv_bits, k_pe_bits, positions, base)
+        deq = e4m3fn_decode(codes) * scale.astype(np.float64)[..., None]
+        d_c = c_kv_bits.shape[-1]
+        return deq[..., :d_c], deq[..., d_c:]
     C = bf16_bits_to_f64(c_kv_bits)
     Kr = rope(bf16_bits_to_f64(k_pe_bits), positions, base)
-    if not fp8:
-        return C, Kr
-    row = np.concatenate([C, Kr], axis=-1).astype(np.float32)
-    codes, scale = fp8_quantize_rows(row)
-    deq = e4m3fn_decode(codes) * scale.astype(np.float64)[..., None]
-    d_c = C.shape[-1]
-    return deq[..., :d_c], deq[..., d_c:]
+    return C, Kr
 
 
 # ----------------------------------------------------------------------------

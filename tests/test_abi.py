@@ -1,0 +1,136 @@
+"""The C ABI on the host (CPU only): the library loads, exports every symbol
+include/mla.h declares, and rejects bad host arguments before enqueueing
+anything.  Every call here fails validation (asserted), so no kernel is ever
+launched with the placeholder pointers used below."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_nope_amd as mla
+from mla_latent_kv_nope_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+lib = _native.lib
+VALIDATION_ERRORS = (_native.MLA_ERR_INVALID_ARG, _native.MLA_ERR_UNSUPPORTED,
+                     _native.MLA_ERR_WORKSPACE)
+P = 0x100000  # aligned placeholder; never dereferenced (validation fails first)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert set(names) == set(_native.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_dims_struct_layout():
+    assert ctypes.sizeof(_native.Dims) == 40
+    assert _native.Dims.rope_base.offset == 32
+
+
+def test_status_strings():
+    for code, name in [(0, "MLA_OK"), (1, "MLA_ERR_INVALID_ARG"), (2, "MLA_ERR_UNSUPPORTED"),
+                       (3, "MLA_ERR_WORKSPACE"), (4, "MLA_ERR_HIP")]:
+        assert mla.status_string(code) == name
+    assert mla.status_string(99) == "MLA_ERR_UNKNOWN"
+
+
+def test_cache_bytes_per_token():
+    assert mla.cache_bytes_per_token(mla.make_dims(128, 512, 64, 128, 128, 64)) == 1152
+    assert mla.cache_bytes_per_token(mla.make_dims(128, 512, 64, 128, 128, 64, fp8=True)) == 580
+    assert mla.cache_bytes_per_token(mla.make_dims(4, 32, 16, 16, 16, 16)) == 96
+    assert lib.mla_cache_bytes_per_token(None) == 0
+
+
+def test_workspace_size():
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    n = lib.mla_decode_workspace_size(ctypes.byref(d), 64, 256)
+    # plan (66 int32) + partial O and lse for 256 + 64 slots, 256-byte aligned pieces
+    assert n >= (256 + 64) * 128 * (512 + 1) * 4
+    assert n < (256 + 64) * 128 * (512 + 1) * 4 + 4096
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 0, 256) == 0
+    bad = mla.make_dims(128, 256, 64, 128, 128, 64)
+    assert lib.mla_decode_workspace_size(ctypes.byref(bad), 4, 8) == 0
+
+
+def _expect(code, want):
+    assert code in VALIDATION_ERRORS, code
+    assert code == want, (mla.status_string(code), mla.status_string(want))
+
+
+def test_append_validation():
+    d = mla.make_dims(4, 32, 16, 16, 16, 16)
+    f = lib.mla_append_latent
+    _expect(f(None, P, P, P, P, P, 2, 4, 10, 5, P, None, 0, None), _native.MLA_ERR_INVALID_ARG)
+    _expect(f(ctypes.byref(d), None, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
+            _native.MLA_ERR_INVALID_ARG)
+    _expect(f(ctypes.byref(d), P, P, P, P, P, 2, 4, 10, -1, P, None, 0, None),
+            _native.MLA_ERR_INVALID_ARG)
+    _expect(f(ctypes.byref(d), P, P, P, P, P, 2, 4, 10, 5, P, None, 7, None),
+            _native.MLA_ERR_INVALID_ARG)                                  # unknown flag
+    _expect(f(ctypes.byref(d), P + 2, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
+            _native.MLA_ERR_INVALID_ARG)                                  # misaligned c_kv
+    _expect(f(ctypes.byref(d), P, P, P, P, P, 2, 4, 10, 5, P, P, 0, None),
+            _native.MLA_ERR_INVALID_ARG)                                  # scales on bf16
+    d8 = mla.make_dims(4, 32, 16, 16, 16, 16, fp8=True)
+    _expect(f(ctypes.byref(d8), P, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
+            _native.MLA_ERR_INVALID_ARG)                                  # fp8 without scales
+    odd_ps = mla.make_dims(4, 32, 16, 16, 16, 24)
+    _expect(f(ctypes.byref(odd_ps), P, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
+            _native.MLA_ERR_UNSUPPORTED)
+    odd_dims = mla.make_dims(4, 64, 16, 16, 16, 16)
+    _expect(f(ctypes.byref(odd_dims), P, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
+            _native.MLA_ERR_UNSUPPORTED)
+    # zero tokens is a no-op that succeeds without touching anything
+    assert f(ctypes.byref(d), None, None, None, None, None, 2, 4, 10, 0, None, None, 0, None) == 0
+
+
+def test_absorb_and_out_proj_validation():
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    _expect(lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, 0, P, None), _native.MLA_ERR_INVALID_ARG)
+    _expect(lib.mla_absorb_q(ctypes.byref(d), P, P, None, P, 4, P, None),
+            _native.MLA_ERR_INVALID_ARG)
+    _expect(lib.mla_absorb_q(ctypes.byref(d), P, P, P, P + 8, 4, P, None),
+            _native.MLA_ERR_INVALID_ARG)
+    too_many = mla.make_dims(129, 512, 64, 128, 128, 64)
+    _expect(lib.mla_absorb_q(ctypes.byref(too_many), P, P, P, P, 4, P, None),
+            _native.MLA_ERR_UNSUPPORTED)
+    _expect(lib.mla_out_proj(ctypes.byref(d), P, None, 4, P, None), _native.MLA_ERR_INVALID_ARG)
+    _expect(lib.mla_out_proj(ctypes.byref(d), P, P, -3, P, None), _native.MLA_ERR_INVALID_ARG)
+
+
+def test_decode_validation():
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    f = lib.mla_decode_paged
+    need = lib.mla_decode_workspace_size(ctypes.byref(d), 4, 8)
+    args = dict(q=P, pool=P, scales=None, bt=P, maxp=8, nump=40, sl=P, B=4, ns=8, ws=P, wsb=need,
+                o=P, lse=P)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(ctypes.byref(d), a["q"], a["pool"], a["scales"], a["bt"], a["maxp"], a["nump"],
+                 a["sl"], a["B"], a["ns"], a["ws"], a["wsb"], a["o"], a["lse"], None)
+
+    _expect(call(wsb=need - 1), _native.MLA_ERR_WORKSPACE)
+    _expect(call(ws=P + 16), _native.MLA_ERR_INVALID_ARG)         # workspace not 256-aligned
+    _expect(call(q=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(B=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(ns=-1), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(scales=P), _native.MLA_ERR_INVALID_ARG)         # scales with a bf16 cache
+    _expect(call(maxp=0), _native.MLA_ERR_INVALID_ARG)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    d = mla.make_dims(4, 32, 16, 16, 16, 16)
+    with pytest.raises(ValueError):
+        mla.out_proj(d, torch.zeros(2, 4, 32, dtype=torch.bfloat16),
+                     torch.zeros(4, 32, 16, dtype=torch.bfloat16))

@@ -1,0 +1,179 @@
+"""mla_decode_paged (and the whole append -> absorb -> decode -> out_proj path)
+on the GPU against the fp64 oracle's explicit, un-absorbed form.
+
+Bar (bf16 inputs, fp32 accumulation), over each compared tensor:
+max |gpu - oracle| <= 2e-2 and ||gpu - oracle|| / ||oracle|| <= 5e-3.
+Block-table gathers are checked bit-exactly with a delta query.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_nope_amd as mla
+from oracle import latent_attention, reference_decode, sequence_rows
+from workload import configs, make_inputs
+from workload.torch_io import bf16_bits, bf16_tensor, i32_tensor
+
+from gpu_util import DEV, assert_close, build_cache, decode_step, dims_for
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    configs.TINY,
+    configs.V2LITE.with_(name="v2lite_S300", seq_len=300),
+    configs.V2LITE.with_(name="v2lite_ragged", seq_len=None, seq_lens=tuple(range(1, 161, 10))),
+    configs.V2LITE.with_(name="v2lite_p16", seq_len=None, seq_lens=(1, 15, 16, 17, 31, 32, 33, 700,
+                                                                    64, 65, 100, 5, 2, 3, 4, 129),
+                         page_size=16),
+    configs.V3.with_(name="v3_small", batch=5, seq_len=None, seq_lens=(1, 31, 32, 33, 1500)),
+    configs.V3.with_(name="v3_h40", batch=3, n_heads=40, seq_len=None, seq_lens=(64, 77, 1)),
+]
+
+
+def _compare(inp, res, batches=None, heads=None):
+    ref = reference_decode(inp, batches=batches, heads=heads)
+    bsel = slice(None) if batches is None else list(batches)
+    hsel = slice(None) if heads is None else list(heads)
+    out = res["out"][bsel][:, hsel]
+    o_lat = res["o_lat"][bsel][:, hsel]
+    lse = res["lse"][bsel][:, hsel]
+    a = assert_close(out, ref["out"], "out")
+    b = assert_close(o_lat, ref["o_lat"], "o_lat")
+    assert np.max(np.abs(lse - ref["lse"])) <= 1e-2, np.max(np.abs(lse - ref["lse"]))
+    return a, b
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_end_to_end_matches_oracle(wl):
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    print(f"[decode e2e] {wl.name}", flush=True)
+    res = decode_step(inp, d)
+    _compare(inp, res)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 0])
+def test_split_invariance(num_splits):
+    wl = configs.V2LITE.with_(name="v2lite_splits", seq_len=None,
+                              seq_lens=(1000, 33, 1, 2047, 64, 500, 300, 129,
+                                        1000, 33, 1, 2047, 64, 500, 300, 129))
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    print(f"[decode splits] num_splits={num_splits}", flush=True)
+    base = decode_step(inp, d, num_splits=1)
+    res = decode_step(inp, d, num_splits=num_splits)
+    rel = np.linalg.norm(res["o_lat"] - base["o_lat"]) / np.linalg.norm(base["o_lat"])
+    assert rel <= 2e-3, rel
+    assert np.max(np.abs(res["lse"] - base["lse"])) <= 1e-5
+    _compare(inp, res)
+
+
+def test_deterministic():
+    wl = configs.V2LITE.with_(name="v2lite_det", seq_len=1111)
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    a = decode_step(inp, d, cache=(pool, scales, t))
+    b = decode_step(inp, d, cache=(pool, scales, t))
+    assert np.array_equal(bf16_bits(a["o_lat_dev"]), bf16_bits(b["o_lat_dev"]))
+    assert np.array_equal(a["lse"], b["lse"])
+
+
+def test_empty_and_single_token_sequences():
+    wl = configs.V2LITE.with_(name="v2lite_empty", batch=4, seq_len=None, seq_lens=(5, 1, 9, 70))
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    q = mla.absorb_q(d, t["q_nope"], t["q_pe"], t["q_pos"], t["w_uk"])
+    seq_lens = i32_tensor(np.array([0, 1, 0, 70]), DEV)
+    o_lat, lse = mla.decode_paged(d, q, pool, scales, t["block_table"], seq_lens)
+    torch.cuda.synchronize()
+    o = o_lat.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    assert np.all(o[[0, 2]] == 0) and np.all(np.isneginf(l[[0, 2]]))
+    # a single token: softmax weight 1, o_lat is that token's latent exactly
+    assert np.array_equal(bf16_bits(o_lat)[1], np.broadcast_to(inp.c_kv[inp.cu_seqlens[1]], (16, 512)))
+    assert np.all(np.isfinite(o[[1, 3]]))
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_delta_query_gathers_bit_exact(num_splits):
+    # c_kv[:, 0] = 0 except 1 at t*; q = A e_0 with softmax_scale * A * log2(e) > 149,
+    # so every other token's weight underflows to 0 and o_lat must equal c_kv[t*]
+    wl = configs.V2LITE.with_(name="v2lite_delta", batch=4, seq_len=None, seq_lens=(300, 1, 4096, 77))
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    c = inp.c_kv.copy()
+    c[:, 0] = 0
+    stars = [299, 0, 2500, 40]
+    for b, ts in enumerate(stars):
+        c[inp.cu_seqlens[b] + ts, 0] = 0x3F80          # 1.0
+    inp.c_kv = c
+    pool, scales, t = build_cache(inp, d)
+    q = np.zeros((wl.batch, wl.n_heads, wl.d_c + wl.d_rope), np.uint16)
+    q[:, :, 0] = 0x44D0                                  # 1664.0
+    o_lat, lse = mla.decode_paged(d, bf16_tensor(q, DEV), pool, scales, t["block_table"],
+                                  t["seq_lens"], num_splits=num_splits)
+    torch.cuda.synchronize()
+    got = bf16_bits(o_lat)
+    for b, ts in enumerate(stars):
+        want = c[inp.cu_seqlens[b] + ts]
+        assert np.array_equal(got[b], np.broadcast_to(want, got[b].shape)), b
+
+
+def test_nan_in_unused_slots_never_reaches_output():
+    # build_cache poisons every slot with NaN before appending; sequences end
+    # mid-page and spare pages stay NaN
+    wl = configs.V2LITE.with_(name="v2lite_nan", seq_len=None, seq_lens=tuple(range(3, 3 + 16 * 37, 37)))
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    res = decode_step(inp, d)
+    assert np.all(np.isfinite(res["out"])) and np.all(np.isfinite(res["o_lat"]))
+    _compare(inp, res)
+
+
+def test_decode_only_with_oracle_query():
+    # drive mla_decode_paged with a query computed by the oracle (rounded to
+    # bf16) and compare o_lat with the oracle's latent attention
+    from oracle import absorb_query, bf16_bits_to_f64
+    from workload import f32_to_bf16_bits
+    wl = configs.V3.with_(name="v3_decode_only", batch=3, seq_len=None, seq_lens=(4000, 1, 129))
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    qo = absorb_query(bf16_bits_to_f64(inp.q_nope), bf16_bits_to_f64(inp.q_pe),
+                      bf16_bits_to_f64(inp.w_uk), inp.q_pos(), wl.rope_base)
+    qb = f32_to_bf16_bits(qo.astype(np.float32))
+    o_lat, lse = mla.decode_paged(d, bf16_tensor(qb, DEV), pool, scales, t["block_table"], t["seq_lens"])
+    torch.cuda.synchronize()
+    got = o_lat.float().cpu().numpy()
+    for b in range(wl.batch):
+        C, Kr = sequence_rows(inp, b)
+        ref, ref_lse = latent_attention(bf16_bits_to_f64(qb[b]), C, Kr, wl.softmax_scale)
+        assert_close(got[b].astype(np.float64), ref, f"o_lat[{b}]")
+        assert np.max(np.abs(lse.cpu().numpy()[b] - ref_lse)) <= 1e-2
+
+
+# ---- full-size workloads, in the launch configuration the benchmark uses ----
+@pytest.mark.slow
+def test_v3_full_size_sampled():
+    wl = configs.V3
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    print("[decode v3 full] B=64 H=128 S=8192", flush=True)
+    res = decode_step(inp, d)
+    assert np.all(np.isfinite(res["out"]))
+    _compare(inp, res, batches=[0, 31, 63])
+
+
+@pytest.mark.slow
+def test_ragged_full_size_sampled():
+    wl = configs.RAGGED
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    order = np.argsort(inp.seq_lens)
+    pick = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    print(f"[decode ragged full] B=128 total={inp.total_tokens} pick={pick}", flush=True)
+    res = decode_step(inp, d)
+    assert np.all(np.isfinite(res["out"]))
+    _compare(inp, res, batches=pick)
