@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v3", choices=["v3", "v2lite", "ragged", "fp8long"])
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=2,
+    ap.add_argument("--cpu-sample", type=int, default=24,
                     help="sequences of the workload the oracle decodes for cpu_baseline (0 = skip)")
     return ap.parse_args()
 

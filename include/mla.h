@@ -196,6 +196,10 @@ size_t mla_cache_bytes_per_token(const mla_dims_t* dims);
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
+/* Description of the HIP error behind the calling thread's most recent
+ * MLA_ERR_HIP (static storage; "no HIP error" if there was none). */
+const char* mla_last_hip_error(void);
+
 /*
  * Kernel timing hooks for benchmarks (not part of the method).
  * mla_profile_begin(n) creates n pairs of HIP events; while active, each

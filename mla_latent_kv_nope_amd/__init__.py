@@ -1,12 +1,20 @@
 """MI355X-native MLA absorbed decode over a paged latent cache.
 
 The compute lives in libmla.so (HIP kernels for gfx950 behind the C ABI of
-include/mla.h); this package is its Python binding.  Importing it loads the
-library and fails if it is missing.
+include/mla.h); this package is its Python binding.  The library is loaded on
+first use of any binding attribute, and that use fails (ImportError) if the
+library is missing; `mla_latent_kv_nope_amd.build` builds it.
 """
-from ._native import LIB_PATH, Dims  # noqa: F401
-from .api import (  # noqa: F401
-    MlaError, absorb_q, append_latent, cache_bytes_per_token, decode_paged, decode_workspace_size,
-    make_dims, new_pool, new_workspace, out_proj, pool_shape, profile_begin, profile_end,
-    status_string,
+_API = (
+    "Dims", "LIB_PATH", "MlaError", "absorb_q", "append_latent", "cache_bytes_per_token",
+    "decode_paged", "decode_workspace_size", "make_dims", "new_pool", "new_workspace", "out_proj",
+    "pool_shape", "profile_begin", "profile_end", "status_string",
 )
+__all__ = list(_API)
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import api, _native
+        return getattr(api, name) if hasattr(api, name) else getattr(_native, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

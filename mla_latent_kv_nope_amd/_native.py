@@ -6,6 +6,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# PyTorch wheels bundle their own HIP runtime.  Importing torch first puts that
+# runtime in the process, so libmla's libamdhip64.so.7 dependency resolves to
+# the same copy; loading libmla first would bring in a second HIP runtime that
+# cannot use torch's device pointers and streams.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
 
@@ -38,8 +44,8 @@ MLA_APPEND_NO_ROPE = 1
 
 EXPORTS = (
     "mla_append_latent", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_paged",
-    "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_profile_begin",
-    "mla_profile_end",
+    "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_last_hip_error",
+    "mla_profile_begin", "mla_profile_end",
 )
 
 _P = ctypes.c_void_p
@@ -69,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_cache_bytes_per_token.restype = ctypes.c_size_t
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_hip_error.argtypes = []
+    lib.mla_last_hip_error.restype = ctypes.c_char_p
     lib.mla_profile_begin.argtypes = [_I]
     lib.mla_profile_begin.restype = ctypes.c_int
     lib.mla_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]

@@ -20,7 +20,10 @@ from ._native import Dims, lib
 class MlaError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
-        super().__init__(f"{fn} failed: {status_string(status)}")
+        msg = f"{fn} failed: {status_string(status)}"
+        if status == _native.MLA_ERR_HIP:
+            msg += f" ({lib.mla_last_hip_error().decode()})"
+        super().__init__(msg)
 
 
 def status_string(status: int) -> str:

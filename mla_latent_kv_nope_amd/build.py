@@ -24,6 +24,8 @@ SOURCES = ["mla_api.cpp", "k_append.hip", "k_absorb.hip", "k_decode.hip", "k_out
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    # code object v5 loads on every ROCm runtime a PyTorch wheel may bundle
+    "-mcode-object-version=5",
     "-I", os.path.join(ROOT, "include"),
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -208,9 +208,9 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
   // 1 KB per chunk group (blocked) or 64 bytes per kc (row-major).
   const uint32_t qk_even = lds_off<Cfg>(l16, quad);
   const uint32_t qk_odd = lds_off<Cfg>(l16, 4 + quad);
-  // QK tail (16-wide chunk, row-major layouts only): elements 32*K32 + 4*quad .. +4
-  const uint32_t qk_tail = lds_off<Cfg>(l16, (32 * Cfg::K32 + 4 * quad) >> 3) +
-                           ((32 * Cfg::K32 + 4 * quad) & 7) * 2;
+  // QK tail (16-wide, row-major layouts only): chunk 4*K32 + (quad & 1) of row
+  // l16; lanes with quad >= 2 read the same in-row chunk and discard it
+  const uint32_t qk_tail = lds_off<Cfg>(l16, 4 * Cfg::K32 + (quad & 1));
   // PV transpose reads: source lane 4r+q of its group reads row 4*quad + r (+16),
   // chunk 2cb + q/2, bytes 8*(q%2): one of four bases (cb % 4) plus 1 KB per cb/4
   // (blocked), or one base plus 32 bytes per cb (row-major).
@@ -258,14 +258,17 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
           if constexpr (Cfg::BLOCKED) {
             const int bi = blk / Cfg::CG, bj = blk - bi * Cfg::CG;
             const int rtok = tok0 + 8 * bi;          // first token of the block's 8 rows
-            const char* rb = (ps >= kTile || bi < 2) ? row0 + 8 * bi * ROWB : page_base(rtok);
+            // a block past the sequence end looks nothing up (its page may not exist)
+            const char* rb = rtok >= S ? nullptr
+                             : (ps >= kTile || bi < 2) ? row0 + 8 * bi * ROWB : page_base(rtok);
             const bool ok = rb != nullptr && row0 != nullptr && rtok + ld_r < S;
             src = ok ? rb + bj * 128 + ld_off : fb + bj * 128 + ld_fb;
           } else {
             const int pos = blk * 64 + lane;         // chunk position in the row-major tile
             const int t = pos / CPR;
             const int c = pos - t * CPR;
-            const char* rb = (ps >= kTile || t < 16) ? row0 : page_base(tok0 + 16);
+            const char* rb = (ps >= kTile || t < 16) ? row0
+                             : (tok0 + 16 < S ? page_base(tok0 + 16) : nullptr);
             const bool ok = rb != nullptr && row0 != nullptr && tok0 + t < S;
             src = ok ? rb + ((ps >= kTile || t < 16) ? t : t - 16) * ROWB + c * 16 : fb + c * 16;
           }
@@ -279,7 +282,7 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
 
     // query registers: lane holds head hbase + l16, elements [32kc + 8*quad, +8)
     bf16x8 qreg[Cfg::K32];
-    bf16x4 qtail = {};
+    bf16x8 qtail = {};  // elements [32*K32 + 8*quad, +8) for quad < 2, zero otherwise
     {
       const int h = hbase + l16;
       const bool hv = h < H;
@@ -291,9 +294,9 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
         qreg[kc] = hv ? v : z;
       }
       if constexpr (Cfg::K16) {
-        const bf16x4 v = *reinterpret_cast<const bf16x4*>(qrow + 32 * Cfg::K32 + 4 * quad);
-        const bf16x4 z4 = {};
-        qtail = hv ? v : z4;
+        const bool tv = hv && quad < 2;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * Cfg::K32 + 8 * (quad & 1));
+        qtail = tv ? v : z;
       }
     }
 
@@ -337,9 +340,13 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
           sacc[tbk] = mfma16(av, qreg[kc], sacc[tbk]);
         }
         if constexpr (Cfg::K16) {
-          const bf16x4 av = *reinterpret_cast<const bf16x4*>(tb + qk_tail + tbk * 16 * ROWB);
-          sacc[tbk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, qtail), sacc[tbk], 0, 0, 0);
+          // the last 16 elements as a 32-wide chunk whose upper half is zero on
+          // both operands: one MFMA shape for the whole accumulator chain (a
+          // 16x16x16 MFMA reading this accumulator right after a 16x16x32 one
+          // has been seen to read stale accumulator registers)
+          const bf16x8 z = {};
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(tb + qk_tail + tbk * 16 * ROWB);
+          sacc[tbk] = mfma16(quad < 2 ? av : z, qtail, sacc[tbk]);
         }
       }
       sched_interleave<2 * Cfg::K32 + (Cfg::K16 ? 2 : 0), 1, 3>();
@@ -395,7 +402,7 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
     __syncthreads();
     const bool again = redo != 0;
     __syncthreads();
-    if (!again) break;
+    if (!again || pass > 0) break;   // the second pass starts at the true maximum
     m_use = m_seen;
     }  // pass
 

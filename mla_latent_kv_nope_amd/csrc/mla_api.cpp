@@ -42,7 +42,13 @@ mla_status_t check_dims(const mla_dims_t* d) {
   return MLA_OK;
 }
 
-mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+thread_local const char* g_last_hip_error = "no HIP error";
+
+mla_status_t from_hip(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  g_last_hip_error = hipGetErrorString(e);
+  return MLA_ERR_HIP;
+}
 
 struct Profiler {
   bool active = false;
@@ -69,6 +75,8 @@ const char* mla_status_string(mla_status_t s) {
   }
   return "MLA_ERR_UNKNOWN";
 }
+
+const char* mla_last_hip_error(void) { return g_last_hip_error; }
 
 size_t mla_cache_bytes_per_token(const mla_dims_t* d) {
   if (d == nullptr || d->d_c <= 0 || d->d_rope < 0) return 0;

@@ -134,3 +134,10 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         mla.out_proj(d, torch.zeros(2, 4, 32, dtype=torch.bfloat16),
                      torch.zeros(4, 32, 16, dtype=torch.bfloat16))
+
+
+def test_single_hip_runtime_in_process():
+    # libmla must bind the HIP runtime PyTorch brought in, not a second copy
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(hip) == 1, hip

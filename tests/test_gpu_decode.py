@@ -177,3 +177,25 @@ def test_ragged_full_size_sampled():
     res = decode_step(inp, d)
     assert np.all(np.isfinite(res["out"]))
     _compare(inp, res, batches=pick)
+
+
+@pytest.mark.parametrize("t_star", [0, 15, 16, 17, 30, 31, 36])
+def test_tiny_delta_query_every_tile_row(t_star):
+    # regression: a one-hot key anywhere in a 32-token tile (both 16-row halves,
+    # the 16-wide QK tail of d_c + d_rope = 48) must be the only token attended
+    wl = configs.TINY
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    c = inp.c_kv.copy()
+    c[:, 0] = 0
+    c[t_star, 0] = 0x3F80                                 # sequence 0 holds tokens 0..36
+    inp.c_kv = c
+    pool, scales, t = build_cache(inp, d)
+    q = np.zeros((wl.batch, wl.n_heads, wl.d_c + wl.d_rope), np.uint16)
+    q[:, :, 0] = 0x44D0                                   # 1664.0
+    o_lat, lse = mla.decode_paged(d, bf16_tensor(q, DEV), pool, scales, t["block_table"],
+                                  t["seq_lens"])
+    torch.cuda.synchronize()
+    got = bf16_bits(o_lat)[0]
+    assert np.array_equal(got, np.broadcast_to(c[t_star], got.shape))
+    assert abs(float(lse[0, 0]) - 1664.0 * wl.softmax_scale) < 1e-3
