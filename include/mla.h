@@ -83,7 +83,7 @@ typedef struct {
   int32_t d_v;               /* per-head value width */
   int32_t page_size;         /* tokens per cache page */
   int32_t cache_dtype;       /* mla_cache_dtype_t */
-  float softmax_scale;       /* multiplies the whole score, e.g. 1/sqrt(d_nope + d_rope) */
+  float softmax_scale;       /* > 0; multiplies the whole score, e.g. 1/sqrt(d_nope + d_rope) */
   double rope_base;          /* RoPE base, e.g. 10000 */
 } mla_dims_t;
 

@@ -47,6 +47,16 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // offset by more than that; such a piece is recomputed with its true maximum.
 constexpr float kHeadroom = 64.0f;  // log2 units
 
+// MFMA operand reads kept in flight ahead of their MFMA (QK^T, PV)
+#ifndef MLA_QK_AHEAD
+#define MLA_QK_AHEAD 4
+#endif
+#ifndef MLA_PV_AHEAD
+#define MLA_PV_AHEAD 3
+#endif
+constexpr int kQkAhead = MLA_QK_AHEAD;
+constexpr int kPvAhead = MLA_PV_AHEAD;
+
 template <int DC, int DR, int NW>
 struct DecodeCfg {
   static constexpr int R = DC + DR;
@@ -223,10 +233,14 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
   }
   // Tile loads (blocked): lane l of every 1 KB load fills row l/8 of its block
   // with logical chunk (l%8) ^ (l/8); the per-lane source offset is the same for
-  // every block.
-  const int ld_r = lane >> 3;
-  const uint32_t ld_off = ld_r * ROWB + (((lane & 7) ^ ld_r) * 16);
-  const uint32_t ld_fb = ((lane & 7) ^ ld_r) * 16;   // same chunk of the block's first row
+  // every block.  Recomputed per tile (see lane_id_fresh) to keep registers free.
+  struct LdLane { int r; uint32_t off, fb; };
+  auto ld_lane = [&]() -> LdLane {
+    const int l = lane_id_fresh();
+    const int r = l >> 3;
+    const uint32_t c16 = (((l & 7) ^ r) * 16);
+    return {r, r * ROWB + c16, c16};   // fb: same chunk of the block's first row
+  };
 
   while (g < gend) {
     const int t0 = plan[b], t1 = plan[b + 1];
@@ -245,11 +259,12 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
       return (pg >= 0 && pg < a.num_pages) ? pool + pg * page_bytes + (tok & (ps - 1)) * ROWB
                                            : nullptr;
     };
-    auto issue_tile = [&](int lt, int buf) {
-      const int tok0 = lt * kTile;
+    auto issue_general = [&](int tok0, char* dst_tile) {
+      const LdLane ll = ld_lane();
+      const int ld_r = ll.r;
+      const uint32_t ld_off = ll.off, ld_fb = ll.fb;
       const char* row0 = page_base(tok0);
       const char* fb = row0 ? row0 : pool;
-      char* dst_tile = lds + buf * Cfg::TILE_BYTES;
 #pragma unroll
       for (int k = 0; k < Cfg::LD_HI; ++k) {
         const int blk = k * NW + wave;               // 1 KB block of the tile this load fills
@@ -264,7 +279,7 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
             const bool ok = rb != nullptr && row0 != nullptr && rtok + ld_r < S;
             src = ok ? rb + bj * 128 + ld_off : fb + bj * 128 + ld_fb;
           } else {
-            const int pos = blk * 64 + lane;         // chunk position in the row-major tile
+            const int pos = blk * 64 + lane_id_fresh();  // chunk position in the row-major tile
             const int t = pos / CPR;
             const int c = pos - t * CPR;
             const char* rb = (ps >= kTile || t < 16) ? row0
@@ -278,6 +293,36 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
               16, 0, 0);
         }
       }
+    };
+    auto issue_tile = [&](int lt, int buf) {
+      const int tok0 = lt * kTile;
+      char* dst_tile = lds + buf * Cfg::TILE_BYTES;
+      if constexpr (Cfg::BLOCKED) {
+        // Fast path: a whole tile of valid tokens inside one page is one
+        // contiguous run; every load is (scalar block base) + (the lane's fixed
+        // offset), with nothing to select per lane.
+        if (ps >= kTile && tok0 + kTile <= S) {
+          const int pg = bt[tok0 >> lg];
+          if (pg >= 0 && pg < a.num_pages) {
+            const char* tile0 = pool + pg * page_bytes + (tok0 & (ps - 1)) * ROWB;
+            const uint32_t ld_off = ld_lane().off;
+#pragma unroll
+            for (int k = 0; k < Cfg::LD_HI; ++k) {
+              const int blk = k * NW + wave;
+              if (blk < Cfg::INSTR) {
+                const int bi = blk / Cfg::CG, bj = blk - bi * Cfg::CG;
+                const char* blk_base = tile0 + (8 * bi * ROWB + bj * 128);
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const void*>(blk_base + ld_off),
+                    reinterpret_cast<lds_void_t*>(reinterpret_cast<uintptr_t>(dst_tile + blk * 1024)),
+                    16, 0, 0);
+              }
+            }
+            return;
+          }
+        }
+      }
+      issue_general(tok0, dst_tile);
     };
 
     // query registers: lane holds head hbase + l16, elements [32kc + 8*quad, +8)
@@ -310,89 +355,148 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
     l_part = 0.f;
     bool overflow = false;
 
-    // prologue: put the first NBUF-1 tiles in flight
+    // Software pipeline over tiles: iteration `it` computes S(it) = K(it).Q^T,
+    // then PV(it - 1) (P of the previous tile, V from its still-resident ring
+    // slot) interleaved with the softmax of S(it).  Two ring slots are read per
+    // iteration, so AHEAD = NBUF - 2 tiles are in flight.
+    constexpr int AHEAD = Cfg::NBUF - 2;
+    static_assert(AHEAD >= 1, "ring too small");
 #pragma unroll
-    for (int i = 0; i < Cfg::NBUF - 1; ++i)
+    for (int i = 0; i < AHEAD; ++i)
       if (i < ntiles) issue_tile(lt0 + i, i);
 
-    for (int it = 0; it < ntiles; ++it) {
-      const int pending = min(ntiles - 1 - it, Cfg::NBUF - 2);
-      if (hi_loader) wait_tiles<Cfg::NBUF, Cfg::LD_HI>(pending);
-      else wait_tiles<Cfg::NBUF, Cfg::LD_LO>(pending);
-      block_barrier();
-      if (it + Cfg::NBUF - 1 < ntiles)
-        issue_tile(lt0 + it + Cfg::NBUF - 1, (it + Cfg::NBUF - 1) % Cfg::NBUF);
-
-      const char* tb = lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES;
-      const int tok0 = (lt0 + it) * kTile;
-
-      // ---- S^T = K_tile . Q^T; token block tb: A operand = row 16tb + l16,
-      // 16-byte chunk 4kc + quad.  Rows l16 and 16 + l16 swizzle alike, and the
-      // swizzled chunk of kc is an even/odd base plus 8*(kc/2) chunks.
-      f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    // ---- S^T = K_tile . Q^T.  MFMA i covers chunk kc = i/2 of token block
+    // tbk = i%2 (two independent accumulator chains, interleaved).  A operand =
+    // row 16tbk + l16, 16-byte chunk 4kc + quad: an even/odd base plus
+    // immediates.  Operands are read QD MFMAs ahead through a rotating set of
+    // registers; sched_barrier pins the issue order.
+    auto qk = [&](const char* tb, f32x4* sacc) {
+      sacc[0] = f32x4{};
+      sacc[1] = f32x4{};
+      constexpr int NQ = 2 * Cfg::K32;
+      constexpr int QD = NQ < kQkAhead ? NQ : kQkAhead;
+      auto a_ptr = [&](int i) {
+        const int kc = i >> 1, tbk = i & 1;
+        return reinterpret_cast<const bf16x8*>(
+            tb + ((kc & 1) ? qk_odd : qk_even) + tbk * 16 * ROWB +
+            (Cfg::BLOCKED ? 1024 * (kc >> 1) : 64 * (kc & ~1)));
+      };
+      bf16x8 abuf[QD];
 #pragma unroll
-      for (int tbk = 0; tbk < 2; ++tbk) {
+      for (int i = 0; i < QD; ++i) abuf[i] = *a_ptr(i);
 #pragma unroll
-        for (int kc = 0; kc < Cfg::K32; ++kc) {
-          const char* ap = tb + ((kc & 1) ? qk_odd : qk_even) + tbk * 16 * ROWB +
-                           (Cfg::BLOCKED ? 1024 * (kc >> 1) : 64 * (kc & ~1));
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(ap);
-          sacc[tbk] = mfma16(av, qreg[kc], sacc[tbk]);
-        }
-        if constexpr (Cfg::K16) {
-          // the last 16 elements as a 32-wide chunk whose upper half is zero on
-          // both operands: one MFMA shape for the whole accumulator chain (a
-          // 16x16x16 MFMA reading this accumulator right after a 16x16x32 one
-          // has been seen to read stale accumulator registers)
-          const bf16x8 z = {};
+      for (int i = 0; i < NQ; ++i) {
+        sacc[i & 1] = mfma16(abuf[i % QD], qreg[i >> 1], sacc[i & 1]);
+        if (i + QD < NQ) abuf[i % QD] = *a_ptr(i + QD);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (Cfg::K16) {
+        // the last 16 elements as a 32-wide chunk whose upper half is zero on
+        // both operands: one MFMA shape for the whole accumulator chain (a
+        // 16x16x16 MFMA reading this accumulator right after a 16x16x32 one
+        // has been seen to read stale accumulator registers)
+        const bf16x8 z = {};
+#pragma unroll
+        for (int tbk = 0; tbk < 2; ++tbk) {
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(tb + qk_tail + tbk * 16 * ROWB);
           sacc[tbk] = mfma16(quad < 2 ? av : z, qtail, sacc[tbk]);
         }
       }
-      sched_interleave<2 * Cfg::K32 + (Cfg::K16 ? 2 : 0), 1, 3>();
+    };
 
-      // ---- online softmax; sacc[tb][i] is token 16tb + 4*quad + i, head l16
+    // ---- online softmax of one tile; sacc[tb][i] is token 16tb + 4*quad + i,
+    // head l16.  Returns P as the PV A operand: k slot 8*quad + j <-> token
+    // (j < 4 ? 4quad + j : 16 + 4quad + j - 4).
+    auto softmax = [&](const f32x4* sacc, int tok0, bool set_offset) -> bf16x8 {
       float x[8];
-      float mt = -INFINITY;
+      float mt;
+      if (tok0 + kTile <= S) {                    // whole tile valid: no mask
 #pragma unroll
-      for (int tbk = 0; tbk < 2; ++tbk)
+        for (int tbk = 0; tbk < 2; ++tbk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * tbk + 4 * quad + i;
-          const float v = (tok0 + t < S) ? sacc[tbk][i] * a.scale_log2 : -INFINITY;
-          x[4 * tbk + i] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = max_across_half_waves(max_across_quarter_pairs(mt));
-      m_seen = fmaxf(m_seen, mt);
-      if (pass == 0 && it == 0) m_use = mt;       // first tile sets the offset; O is still zero
-      overflow |= mt > m_use + kHeadroom;
-      float p[8];
+          for (int i = 0; i < 4; ++i) x[4 * tbk + i] = sacc[tbk][i];
+        mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      } else {
+        mt = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = exp2f(x[j] - m_use);
-        l_part += p[j];
+        for (int tbk = 0; tbk < 2; ++tbk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * tbk + 4 * quad + i;
+            const float v = (tok0 + t < S) ? sacc[tbk][i] : -INFINITY;
+            x[4 * tbk + i] = v;
+            mt = fmaxf(mt, v);
+          }
       }
-      // PV A operand: k slot 8*quad + j <-> token (j < 4 ? 4quad + j : 16 + 4quad + j - 4)
+      // scores are raw dot products here; the base-2 scale is applied once to
+      // the maximum and fused into the exponent argument below
+      mt = max_across_half_waves(max_across_quarter_pairs(mt)) * a.scale_log2;
+      m_seen = fmaxf(m_seen, mt);
+      if (set_offset) m_use = mt;                 // first tile: O is still zero
+      overflow |= mt > m_use + kHeadroom;
       uint32_t pu[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pu[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, pu);
+      for (int j = 0; j < 4; ++j) {
+        // v_exp_f32 directly: arguments <= kHeadroom, results below 2^-126 of
+        // the maximum may flush to zero
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j], a.scale_log2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j + 1], a.scale_log2, -m_use));
+        l_part += p0 + p1;
+        pu[j] = pack_bf16x2(p0, p1);
+      }
+      return __builtin_bit_cast(bf16x8, pu);
+    };
 
-      // ---- O += P . V_tile.  Transpose-read source lane 4r+q of group `quad`
-      // reads token rows 4*quad + r and 16 + 4*quad + r at channels 16cb + 4q;
-      // the swizzled address is one of four bases (by cb % 4) plus immediates.
-#pragma unroll
-      for (int cb = 0; cb < Cfg::VCB; ++cb) {
+    // ---- O += P . V_tile.  Transpose-read source lane 4r+q of group `quad`
+    // reads token rows 4*quad + r and 16 + 4*quad + r at channels 16cb + 4q;
+    // the swizzled address is one of four bases (by cb % 4) plus immediates.
+    // B operands are read PD MFMAs ahead; the scheduler may interleave the
+    // independent softmax VALU work of the next tile between these MFMAs.
+    auto pv = [&](const char* tb, bf16x8 pa) {
+      constexpr int PD = Cfg::VCB < kPvAhead ? Cfg::VCB : kPvAhead;
+      auto v_read = [&](int cb) {
         const int imm = Cfg::BLOCKED ? 1024 * (cb >> 2) : 32 * cb;
         const char* p0 = tb + (Cfg::BLOCKED ? pv_base[cb & 3] : pv_base[0]) + imm;
         const bf16x4 v0 = lds_read_tr16(p0);
         const bf16x4 v1 = lds_read_tr16(p0 + 16 * ROWB);
-        const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[cb] = mfma16(pa, bv, o[cb]);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 vbuf[PD];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) vbuf[i] = v_read(i);
+#pragma unroll
+      for (int cb = 0; cb < Cfg::VCB; ++cb) {
+        o[cb] = mfma16(pa, vbuf[cb % PD], o[cb]);
+        if (cb + PD < Cfg::VCB) vbuf[cb % PD] = v_read(cb + PD);
       }
-      sched_interleave<Cfg::VCB, 2, 2>();
+      sched_interleave<Cfg::VCB, 2, PD>();
+    };
+
+    auto wait_and_sync = [&](int it) {
+      const int pending = min(ntiles - 1 - it, AHEAD - 1);
+      if (hi_loader) wait_tiles<AHEAD + 2, Cfg::LD_HI>(pending);
+      else wait_tiles<AHEAD + 2, Cfg::LD_LO>(pending);
+      block_barrier();
+      if (it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
+    };
+
+    f32x4 sacc[2];
+    bf16x8 pa;
+    // first tile: QK + softmax (sets the exponent offset on the first pass)
+    wait_and_sync(0);
+    qk(lds, sacc);
+    pa = softmax(sacc, lt0 * kTile, pass == 0);
+    for (int it = 1; it < ntiles; ++it) {
+      wait_and_sync(it);
+      const char* tb = lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES;
+      qk(tb, sacc);
+      const bf16x8 pa_prev = pa;
+      pv(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, pa_prev);
+      pa = softmax(sacc, (lt0 + it) * kTile, false);
     }
+    // last tile's PV (its ring slot is not refilled: no later loads)
+    pv(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, pa);
 
     // a score far above the offset anywhere in the workgroup: redo the piece
     // with each head's true maximum as its offset (cannot overflow again)

@@ -32,7 +32,7 @@ mla_status_t check_dims(const mla_dims_t* d) {
   if (d->cache_dtype != MLA_CACHE_BF16 && d->cache_dtype != MLA_CACHE_FP8_E4M3)
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(d->rope_base) || d->rope_base <= 0.0) return MLA_ERR_INVALID_ARG;
-  if (!std::isfinite(d->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   const bool v3 = d->d_c == 512 && d->d_rope == 64 && d->d_nope == 128 && d->d_v == 128;
   const bool tiny = d->d_c == 32 && d->d_rope == 16 && d->d_nope == 16 && d->d_v == 16;
   if (!v3 && !tiny) return MLA_ERR_UNSUPPORTED;

@@ -93,6 +93,15 @@ __device__ __forceinline__ float sum_across_quarter_pairs(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Lane index recomputed at each use (two VALU ops).  The volatile asm keeps the
+// compiler from hoisting values derived from it out of loops, which trades a
+// few instructions for registers that would otherwise stay occupied.
+__device__ __forceinline__ int lane_id_fresh() {
+  int l;
+  __asm__ __volatile__("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ float shfl_f32(float x, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
 }

@@ -86,6 +86,9 @@ def test_append_validation():
     odd_ps = mla.make_dims(4, 32, 16, 16, 16, 24)
     _expect(f(ctypes.byref(odd_ps), P, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
             _native.MLA_ERR_UNSUPPORTED)
+    neg_scale = mla.make_dims(4, 32, 16, 16, 16, 16, softmax_scale=-0.5)
+    _expect(f(ctypes.byref(neg_scale), P, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
+            _native.MLA_ERR_INVALID_ARG)
     odd_dims = mla.make_dims(4, 64, 16, 16, 16, 16)
     _expect(f(ctypes.byref(odd_dims), P, P, P, P, P, 2, 4, 10, 5, P, None, 0, None),
             _native.MLA_ERR_UNSUPPORTED)
