@@ -13,11 +13,12 @@
 //             sums, and the per-workgroup quota = ceil(total tiles / parts).
 //   k_split   workgroup w takes global tiles [w*quota, (w+1)*quota) of the
 //             concatenated batch; a range may cover the tail of one sequence
-//             and the head of the next.  For every (w, b) piece it streams the
-//             tiles and writes either the final o_lat/lse (the piece is the
-//             whole sequence) or a normalised partial O and its lse to slot
-//             w + b of the workspace.
-//   k_combine merges the partial pieces of every split sequence.
+//             and the head of the next.  A piece that is a whole sequence
+//             writes o_lat/lse directly; otherwise the piece's normalised O
+//             (fp32) and lse go to slot w + b of the workspace.
+//   k_combine merges the pieces of every split sequence by their log-sum-exp,
+//             in piece order, and writes o_lat = 0, lse = -inf for sequences
+//             with no tokens.
 //
 // k_split design (gfx950): a workgroup of NW waves x 16 heads works on one
 // (sequence piece, head group); with NW = 8 one workgroup holds all 128 heads, so
@@ -85,6 +86,7 @@ struct DecodeCfg {
   static_assert(R % 16 == 0 && DC % 16 == 0, "dims");
   static_assert((kTile * CPR) % 64 == 0, "tile load split");
   static_assert((NBUF - 2) * LD_HI <= 63, "vmcnt range");
+  static_assert(!BLOCKED || TILE_BYTES % 1024 == 0, "blocked tiles keep the low 10 address bits free");
 };
 
 // byte offset of (row t, 16-byte chunk c) inside a tile buffer
@@ -179,6 +181,10 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
   // the compiler prove nothing here writes them); scalar loads wait on their
   // own counter, so they never force a wait for the in-flight tile loads.
   const int B = a.B, H = a.H;
+  const int HG16 = (H + 15) >> 4;                  // 16-head groups (partial O layout)
+  const int cap = a.max_pages << a.page_size_log2;
+
+
   const int total = plan[B];
   const int quota = plan[B + 1];
   int g = w * quota;
@@ -191,7 +197,6 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
   const int l16 = lane & 15;
   const int lg = a.page_size_log2;
   const int ps = 1 << lg;
-  const int cap = a.max_pages << lg;
   const int hbase = (hg * NW + wave) * 16;   // first head of this wave
   constexpr int REM = Cfg::INSTR % NW;
   const bool hi_loader = REM == 0 || wave < REM;
@@ -213,24 +218,33 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
   }
 
   // Per-lane LDS byte offsets (relative to a tile buffer) of the MFMA operand
-  // reads; every other operand address is one of these plus an immediate.
+  // reads; every other operand address is one of these plus an immediate.  They
+  // are recomputed from lane_id_fresh at each tile (a handful of VALU ops) so
+  // that no register is held for them across the tile loop.
   // QK: row l16 (+16 per token block), chunk 4kc + quad: an even/odd base plus
-  // 1 KB per chunk group (blocked) or 64 bytes per kc (row-major).
-  const uint32_t qk_even = lds_off<Cfg>(l16, quad);
-  const uint32_t qk_odd = lds_off<Cfg>(l16, 4 + quad);
-  // QK tail (16-wide, row-major layouts only): chunk 4*K32 + (quad & 1) of row
-  // l16; lanes with quad >= 2 read the same in-row chunk and discard it
-  const uint32_t qk_tail = lds_off<Cfg>(l16, 4 * Cfg::K32 + (quad & 1));
+  // 1 KB per chunk group (blocked) or 64 bytes per kc (row-major).  In the
+  // blocked layout the odd base is the even one with chunk bit 2 flipped.
+  struct QkBases { uint32_t even, odd, tail; };
+  auto qk_bases = [&]() -> QkBases {
+    const int l = lane_id_fresh();
+    const int r = l & 15, q = l >> 4;
+    QkBases qb;
+    qb.even = lds_off<Cfg>(r, q);
+    qb.odd = Cfg::BLOCKED ? (qb.even ^ 64u) : lds_off<Cfg>(r, 4 + q);
+    // QK tail (16-wide, row-major layouts only): chunk 4*K32 + (quad & 1) of
+    // row l16; lanes with quad >= 2 read the same in-row chunk and discard it
+    qb.tail = Cfg::K16 ? lds_off<Cfg>(r, 4 * Cfg::K32 + (q & 1)) : 0u;
+    return qb;
+  };
   // PV transpose reads: source lane 4r+q of its group reads row 4*quad + r (+16),
-  // chunk 2cb + q/2, bytes 8*(q%2): one of four bases (cb % 4) plus 1 KB per cb/4
-  // (blocked), or one base plus 32 bytes per cb (row-major).
-  uint32_t pv_base[4];
-  {
-    const int trr = l16 >> 2, trq = l16 & 3;
-    const int trow = 4 * quad + trr;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) pv_base[m] = lds_off<Cfg>(trow, 2 * m + (trq >> 1)) + (trq & 1) * 8;
-  }
+  // chunk 2cb + q/2, bytes 8*(q%2).  Blocked: the base for cb % 4 = m is the
+  // base for m = 0 with chunk bits 1-2 xor m, plus 1 KB per cb/4; row-major:
+  // one base plus 32 bytes per cb.
+  auto pv_base0 = [&]() -> uint32_t {
+    const int l = lane_id_fresh();
+    const int trr = (l & 15) >> 2, trq = l & 3;
+    return lds_off<Cfg>(4 * (l >> 4) + trr, trq >> 1) + (trq & 1) * 8;
+  };
   // Tile loads (blocked): lane l of every 1 KB load fills row l/8 of its block
   // with logical chunk (l%8) ^ (l/8); the per-lane source offset is the same for
   // every block.  Recomputed per tile (see lane_id_fresh) to keep registers free.
@@ -375,10 +389,11 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
       sacc[1] = f32x4{};
       constexpr int NQ = 2 * Cfg::K32;
       constexpr int QD = NQ < kQkAhead ? NQ : kQkAhead;
+      const QkBases qb = qk_bases();
       auto a_ptr = [&](int i) {
         const int kc = i >> 1, tbk = i & 1;
         return reinterpret_cast<const bf16x8*>(
-            tb + ((kc & 1) ? qk_odd : qk_even) + tbk * 16 * ROWB +
+            tb + ((kc & 1) ? qb.odd : qb.even) + tbk * 16 * ROWB +
             (Cfg::BLOCKED ? 1024 * (kc >> 1) : 64 * (kc & ~1)));
       };
       bf16x8 abuf[QD];
@@ -398,7 +413,7 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
         const bf16x8 z = {};
 #pragma unroll
         for (int tbk = 0; tbk < 2; ++tbk) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(tb + qk_tail + tbk * 16 * ROWB);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(tb + qb.tail + tbk * 16 * ROWB);
           sacc[tbk] = mfma16(quad < 2 ? av : z, qtail, sacc[tbk]);
         }
       }
@@ -455,9 +470,13 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
     // independent softmax VALU work of the next tile between these MFMAs.
     auto pv = [&](const char* tb, bf16x8 pa) {
       constexpr int PD = Cfg::VCB < kPvAhead ? Cfg::VCB : kPvAhead;
+      // tile buffers are 4 KB aligned, so the xor may be applied after adding
+      // the buffer address
+      const uintptr_t pb = reinterpret_cast<uintptr_t>(tb) + pv_base0();
       auto v_read = [&](int cb) {
         const int imm = Cfg::BLOCKED ? 1024 * (cb >> 2) : 32 * cb;
-        const char* p0 = tb + (Cfg::BLOCKED ? pv_base[cb & 3] : pv_base[0]) + imm;
+        const char* p0 = reinterpret_cast<const char*>(
+                             Cfg::BLOCKED ? (pb ^ static_cast<uintptr_t>(32 * (cb & 3))) : pb) + imm;
         const bf16x4 v0 = lds_read_tr16(p0);
         const bf16x4 v1 = lds_read_tr16(p0 + 16 * ROWB);
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -514,32 +533,48 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
     const float l_tot = sum_across_half_waves(sum_across_quarter_pairs(l_part));
     const float inv = 1.0f / l_tot;
     const float lse_nat = (m_use + log2f(l_tot)) * kLn2;
-    if (whole) {
-      uint16_t* ob = a.o_lat + static_cast<int64_t>(b) * H * DC;
+    // this lane's 4 heads (4*quad + i) scaled by 1 / l
+    f32x4 scv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scv[i] = shfl_f32(inv, 4 * quad + i);
+#pragma unroll
+    for (int cb = 0; cb < Cfg::VCB; ++cb) o[cb] *= scv;
+
+    // o_lat rows of this wave's 16 heads: lane (quad, l16) writes channel
+    // 16cb + l16 of heads 4quad + i at an immediate offset from one of four
+    // lane offsets; heads past H get an offset beyond the buffer's range, whose
+    // stores the hardware drops
+    // (Lane-derived values of the epilogue are recomputed from lane_id_fresh so
+    // that none of them is hoisted into a register held across the tile loop.)
+    auto store_olat = [&]() {
+      const auto rs = make_rsrc(a.o_lat + (static_cast<int64_t>(b) * H + hbase) * DC, 16 * DC * 2);
+      const int fl = lane_id_fresh();
+      const int fq = fl >> 4, f16 = fl & 15;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float sc = shfl_f32(inv, 4 * quad + i);
-        const int h = hbase + 4 * quad + i;
-        if (h < H) {
+        const uint32_t vo = hbase + 4 * fq + i < H
+                                ? static_cast<uint32_t>((4 * fq + i) * DC + f16) * 2 : 0x80000000u;
 #pragma unroll
-          for (int cb = 0; cb < Cfg::VCB; ++cb)
-            ob[static_cast<int64_t>(h) * DC + 16 * cb + l16] = f32_to_bf16_bits(o[cb][i] * sc);
-        }
+        for (int cb = 0; cb < Cfg::VCB; ++cb)
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(o[cb][i])), rs, vo,
+                                                32 * cb, 0);
       }
+    };
+
+    if (whole) {
+      store_olat();
       if (a.lse != nullptr && quad == 0 && hbase + l16 < H)
         a.lse[static_cast<int64_t>(b) * H + hbase + l16] = lse_nat;
     } else {
+      // Partial piece: O (fp32) in this wave's accumulator order, one 16-byte
+      // store per lane and column block, and its lse; k_combine merges them.
       const int64_t slot = static_cast<int64_t>(w) + b;
-      float* po = a.part_o + slot * H * DC;
+      if (hbase < H) {   // waves past the last head have nothing to store
+        constexpr uint32_t kPieceBytes = Cfg::VCB * 64 * 16;   // 16 heads x d_c fp32
+        const auto rs = make_rsrc(a.part_o + (slot * HG16 + (hbase >> 4)) * (kPieceBytes / 4), kPieceBytes);
+        const uint32_t voff = static_cast<uint32_t>(lane_id_fresh()) * 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = shfl_f32(inv, 4 * quad + i);
-        const int h = hbase + 4 * quad + i;
-        if (h < H) {
-#pragma unroll
-          for (int cb = 0; cb < Cfg::VCB; ++cb)
-            po[static_cast<int64_t>(h) * DC + 16 * cb + l16] = o[cb][i] * sc;
-        }
+        for (int cb = 0; cb < Cfg::VCB; ++cb) buffer_store_f32x4(o[cb], rs, voff, cb * 1024);
       }
       if (quad == 0 && hbase + l16 < H) a.part_lse[slot * H + hbase + l16] = lse_nat;
     }
@@ -554,39 +589,119 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
 }
 
 // ---------------------------------------------------------------------------
-// One wave per (b, h): merge the pieces of split sequences; write zeros and
-// -inf for empty sequences.  Pieces computed whole were written by k_split.
-__global__ __launch_bounds__(256) void k_combine(DecodeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int B = a.B, H = a.H, DC = a.d_c;
-  if (bh >= B * H) return;
-  const int b = bh / H, h = bh - b * H;
-  const int t0 = a.plan[b], t1 = a.plan[b + 1];
-  const int quota = a.plan[B + 1];
-  uint16_t* ob = a.o_lat + static_cast<int64_t>(bh) * DC;
+// Merge of split sequences.  One wave per (sequence, 16-head group, 8 column
+// blocks): the pieces' lse give each head's merged lse and the piece weights
+// exp(lse_p - lse); the pieces' O are read in the split kernel's accumulator
+// order (16-byte loads, 1 KB per wave instruction) and summed in piece order.
+// Sequences with no tokens get o_lat = 0 and lse = -inf; whole-sequence pieces
+// were written by k_split.
+template <int DC>
+__global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
+  constexpr int VCB = DC / 16;
+  constexpr int CPW = VCB < 8 ? VCB : 8;   // column blocks per wave
+  constexpr int NQ = VCB / CPW;
+  constexpr uint32_t kPieceBytes = VCB * 64 * 16;
+  const int H = a.H, HG16 = (H + 15) >> 4;
+  int id = blockIdx.x;
+  const int cq = id % NQ;
+  id /= NQ;
+  const int gw = id % HG16;
+  const int b = id / HG16;
+  const int lane = threadIdx.x, quad = lane >> 4, l16 = lane & 15;
+  const int hq = gw * 16 + 4 * quad;       // first of this lane's 4 heads
+  const int t0 = a.plan[b], t1 = a.plan[b + 1], quota = a.plan[a.B + 1];
+
+  // o_lat of this lane's heads: channel 16cb + l16 of heads hq + i; heads
+  // past H get an offset beyond the buffer's range (the store is dropped)
+  const auto ro = make_rsrc(a.o_lat + (static_cast<int64_t>(b) * H + gw * 16) * DC, 16 * DC * 2);
+  auto store = [&](const f32x4* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t vo = hq + i < H ? static_cast<uint32_t>((4 * quad + i) * DC + l16) * 2 : 0x80000000u;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(v[c][i])), ro, vo,
+                                              32 * (cq * CPW + c), 0);
+    }
+  };
+
   if (t1 == t0) {
-    for (int c = lane; c < DC; c += 64) ob[c] = 0;
-    if (a.lse != nullptr && lane == 0) a.lse[bh] = -INFINITY;
+    f32x4 z[CPW] = {};
+    store(z);
+    if (a.lse != nullptr && cq == 0 && l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (hq + i < H) a.lse[static_cast<int64_t>(b) * H + hq + i] = -INFINITY;
+    }
     return;
   }
   const int wf = t0 / quota, wl = (t1 - 1) / quota;
-  if (wf == wl) return;
-  float mx = -INFINITY;
-  for (int wv = wf; wv <= wl; ++wv) mx = fmaxf(mx, a.part_lse[(static_cast<int64_t>(wv) + b) * H + h]);
-  float sum = 0.f;
-  for (int wv = wf; wv <= wl; ++wv) sum += expf(a.part_lse[(static_cast<int64_t>(wv) + b) * H + h] - mx);
-  const float lse_all = mx + logf(sum);
-  for (int c = lane; c < DC; c += 64) {
-    float acc = 0.f;
-    for (int wv = wf; wv <= wl; ++wv) {
-      const int64_t slot = static_cast<int64_t>(wv) + b;
-      const float wgt = expf(a.part_lse[slot * H + h] - lse_all);
-      acc += wgt * a.part_o[(slot * H + h) * DC + c];
-    }
-    ob[c] = f32_to_bf16_bits(acc);
+  if (wf == wl || gw * 16 >= H) return;
+
+  // pieces in groups of PG: every load of a group is issued before any use,
+  // so each group costs one memory round trip
+  constexpr int PG = 4;
+  const int np = wl - wf + 1;
+  const int64_t lse0 = (static_cast<int64_t>(wf) + b) * H;
+  int hc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hc[i] = min(hq + i, H - 1);
+  f32x4 mx = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int k0 = 0; k0 < np; k0 += PG) {
+    f32x4 l[PG];
+#pragma unroll
+    for (int k = 0; k < PG; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l[k][i] = k0 + k < np ? a.part_lse[lse0 + (k0 + k) * H + hc[i]] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < PG; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], l[k][i]);
   }
-  if (a.lse != nullptr && lane == 0) a.lse[bh] = lse_all;
+  f32x4 acc[CPW];
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t voff = static_cast<uint32_t>(lane) * 16;
+  for (int k0 = 0; k0 < np; k0 += PG) {
+    f32x4 t[PG][CPW];
+    f32x4 l[PG];
+#pragma unroll
+    for (int k = 0; k < PG; ++k) {
+      const bool ok = k0 + k < np;
+      const int64_t slot = static_cast<int64_t>(wf + (ok ? k0 + k : 0)) + b;
+      const auto rs = make_rsrc(a.part_o + (slot * HG16 + gw) * (kPieceBytes / 4), kPieceBytes);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) t[k][c] = buffer_load_f32x4(rs, voff, (cq * CPW + c) * 1024);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l[k][i] = ok ? a.part_lse[lse0 + (k0 + k) * H + hc[i]] : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < PG; ++k) {
+      if (k0 + k >= np) break;
+      // unnormalised weights exp(lse_p - max); the sum normalises at the end
+      f32x4 wgt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wgt[i] = expf(l[k][i] - mx[i]);
+      sum += wgt;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) acc[c] = (k0 + k == 0) ? t[k][c] * wgt : acc[c] + t[k][c] * wgt;
+    }
+  }
+  f32x4 inv, lse_all;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    inv[i] = 1.0f / sum[i];
+    lse_all[i] = mx[i] + logf(sum[i]);
+  }
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) acc[c] *= inv;
+  store(acc);
+  if (a.lse != nullptr && cq == 0 && l16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (hq + i < H) a.lse[static_cast<int64_t>(b) * H + hq + i] = lse_all[i];
+  }
 }
 
 template <int DC, int DR, int NW>
@@ -628,7 +743,8 @@ WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {
   L.plan_off = 0;
   L.part_o_off = up(sizeof(int32_t) * (static_cast<size_t>(B) + 2));
   const size_t slots = static_cast<size_t>(num_parts) + B;
-  L.part_lse_off = L.part_o_off + up(sizeof(float) * slots * H * d_c);
+  const size_t hpad = (static_cast<size_t>(H) + 15) / 16 * 16;
+  L.part_lse_off = L.part_o_off + up(sizeof(float) * slots * hpad * d_c);
   L.total = L.part_lse_off + up(sizeof(float) * slots * H);
   return L;
 }
@@ -654,8 +770,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hip
   }
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-  const int waves = a.B * a.H;
-  hipLaunchKernelGGL(k_combine, dim3((waves + 3) / 4), dim3(256), 0, s, a);
+  const int hg16 = (a.H + 15) / 16;
+  if (a.d_c == 512)
+    hipLaunchKernelGGL(k_combine<512>, dim3(a.B * hg16 * 4), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_combine<32>, dim3(a.B * hg16), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -59,6 +59,25 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds_ptr) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// ---- raw buffer access -----------------------------------------------------
+// A buffer resource over [p, p + bytes) in the gfx9 raw (unswizzled) format.
+// Loads and stores through it take a per-lane 32-bit offset plus a uniform
+// offset, so a run of accesses at constant distances needs no 64-bit address
+// per access.  Out-of-range accesses read 0 and drop writes.
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void buffer_store_f32x4(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, static_cast<int>(voff),
+                                         static_cast<int>(soff), 0);
+}
+__device__ __forceinline__ f32x4 buffer_load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+
 // ---- waits and barriers ---------------------------------------------------
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
 template <int N>

@@ -46,8 +46,9 @@ struct OutProjArgs {
 };
 
 // Workspace of mla_decode_paged, carved from the caller's buffer:
-//   plan      int32 [B + 1] tile prefix sums, then int32 quota, total
-//   part_o    fp32 [num_parts + B][H][d_c]  normalised partial outputs
+//   plan      int32 [B + 1] tile prefix sums, then int32 quota
+//   part_o    fp32 [num_parts + B][ceil(H/16)][d_c/16][64][4]  normalised partial
+//             outputs in the decode waves' accumulator order
 //   part_lse  fp32 [num_parts + B][H]
 // A partial computed by workgroup w for sequence b lives in slot w + b.
 struct DecodeArgs {
