@@ -15,7 +15,7 @@
 //             concatenated batch; a range may cover the tail of one sequence
 //             and the head of the next.  A piece that is a whole sequence
 //             writes o_lat/lse directly; otherwise the piece's normalised O
-//             (fp32) and lse go to slot w + b of the workspace.
+//             (bf16) and lse (fp32) go to slot w + b of the workspace.
 //   k_combine merges the pieces of every split sequence by their log-sum-exp,
 //             in piece order, and writes o_lat = 0, lse = -inf for sequences
 //             with no tokens.
@@ -566,15 +566,16 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
       if (a.lse != nullptr && quad == 0 && hbase + l16 < H)
         a.lse[static_cast<int64_t>(b) * H + hbase + l16] = lse_nat;
     } else {
-      // Partial piece: O (fp32) in this wave's accumulator order, one 16-byte
-      // store per lane and column block, and its lse; k_combine merges them.
+      // Partial piece: normalised O rounded to bf16 in this wave's accumulator
+      // order, one 8-byte store per lane and column block, and its lse (fp32);
+      // k_combine merges them.
       const int64_t slot = static_cast<int64_t>(w) + b;
       if (hbase < H) {   // waves past the last head have nothing to store
-        constexpr uint32_t kPieceBytes = Cfg::VCB * 64 * 16;   // 16 heads x d_c fp32
-        const auto rs = make_rsrc(a.part_o + (slot * HG16 + (hbase >> 4)) * (kPieceBytes / 4), kPieceBytes);
-        const uint32_t voff = static_cast<uint32_t>(lane_id_fresh()) * 16;
+        constexpr uint32_t kPieceBytes = Cfg::VCB * 64 * 8;    // 16 heads x d_c bf16
+        const auto rs = make_rsrc(a.part_o + (slot * HG16 + (hbase >> 4)) * (kPieceBytes / 2), kPieceBytes);
+        const uint32_t voff = static_cast<uint32_t>(lane_id_fresh()) * 8;
 #pragma unroll
-        for (int cb = 0; cb < Cfg::VCB; ++cb) buffer_store_f32x4(o[cb], rs, voff, cb * 1024);
+        for (int cb = 0; cb < Cfg::VCB; ++cb) buffer_store_bf16x4(o[cb], rs, voff, cb * 512);
       }
       if (quad == 0 && hbase + l16 < H) a.part_lse[slot * H + hbase + l16] = lse_nat;
     }
@@ -592,7 +593,8 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
 // Merge of split sequences.  One wave per (sequence, 16-head group, 8 column
 // blocks): the pieces' lse give each head's merged lse and the piece weights
 // exp(lse_p - lse); the pieces' O are read in the split kernel's accumulator
-// order (16-byte loads, 1 KB per wave instruction) and summed in piece order.
+// order (bf16, 8-byte loads, 512 bytes per wave instruction) and summed in
+// piece order in fp32.
 // Sequences with no tokens get o_lat = 0 and lse = -inf; whole-sequence pieces
 // were written by k_split.
 template <int DC>
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
   constexpr int VCB = DC / 16;
   constexpr int CPW = VCB < 8 ? VCB : 8;   // column blocks per wave
   constexpr int NQ = VCB / CPW;
-  constexpr uint32_t kPieceBytes = VCB * 64 * 16;
+  constexpr uint32_t kPieceBytes = VCB * 64 * 8;
   const int H = a.H, HG16 = (H + 15) >> 4;
   int id = blockIdx.x;
   const int cq = id % NQ;
@@ -661,7 +663,7 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
   }
   f32x4 acc[CPW];
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t voff = static_cast<uint32_t>(lane) * 16;
+  const uint32_t voff = static_cast<uint32_t>(lane) * 8;
   for (int k0 = 0; k0 < np; k0 += PG) {
     f32x4 t[PG][CPW];
     f32x4 l[PG];
@@ -669,9 +671,9 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
     for (int k = 0; k < PG; ++k) {
       const bool ok = k0 + k < np;
       const int64_t slot = static_cast<int64_t>(wf + (ok ? k0 + k : 0)) + b;
-      const auto rs = make_rsrc(a.part_o + (slot * HG16 + gw) * (kPieceBytes / 4), kPieceBytes);
+      const auto rs = make_rsrc(a.part_o + (slot * HG16 + gw) * (kPieceBytes / 2), kPieceBytes);
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) t[k][c] = buffer_load_f32x4(rs, voff, (cq * CPW + c) * 1024);
+      for (int c = 0; c < CPW; ++c) t[k][c] = buffer_load_bf16x4(rs, voff, (cq * CPW + c) * 512);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         l[k][i] = ok ? a.part_lse[lse0 + (k0 + k) * H + hc[i]] : -INFINITY;
@@ -744,7 +746,7 @@ WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {
   L.part_o_off = up(sizeof(int32_t) * (static_cast<size_t>(B) + 2));
   const size_t slots = static_cast<size_t>(num_parts) + B;
   const size_t hpad = (static_cast<size_t>(H) + 15) / 16 * 16;
-  L.part_lse_off = L.part_o_off + up(sizeof(float) * slots * hpad * d_c);
+  L.part_lse_off = L.part_o_off + up(sizeof(uint16_t) * slots * hpad * d_c);
   L.total = L.part_lse_off + up(sizeof(float) * slots * H);
   return L;
 }

@@ -195,7 +195,7 @@ mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* po
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
-  a.part_o = reinterpret_cast<float*>(ws + L.part_o_off);
+  a.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse_off);
   a.o_lat = static_cast<uint16_t*>(o_lat);
   a.lse = lse;

@@ -77,6 +77,19 @@ __device__ __forceinline__ f32x4 buffer_load_f32x4(__amdgpu_buffer_rsrc_t r, uin
   return __builtin_bit_cast(
       f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0));
 }
+// four fp32 <-> four bf16 (round to nearest even) through an 8-byte access
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+__device__ __forceinline__ void buffer_store_bf16x4(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                    uint32_t soff) {
+  const i32x2 p = {static_cast<int>(pack_bf16x2(v[0], v[1])), static_cast<int>(pack_bf16x2(v[2], v[3]))};
+  __builtin_amdgcn_raw_buffer_store_b64(p, r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+__device__ __forceinline__ f32x4 buffer_load_bf16x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const i32x2 p = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  const uint32_t lo = static_cast<uint32_t>(p[0]), hi = static_cast<uint32_t>(p[1]);
+  return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u), __uint_as_float(hi << 16),
+               __uint_as_float(hi & 0xffff0000u)};
+}
 
 // ---- waits and barriers ---------------------------------------------------
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding).

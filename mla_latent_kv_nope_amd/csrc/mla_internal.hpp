@@ -47,7 +47,7 @@ struct OutProjArgs {
 
 // Workspace of mla_decode_paged, carved from the caller's buffer:
 //   plan      int32 [B + 1] tile prefix sums, then int32 quota
-//   part_o    fp32 [num_parts + B][ceil(H/16)][d_c/16][64][4]  normalised partial
+//   part_o    bf16 [num_parts + B][ceil(H/16)][d_c/16][64][4]  normalised partial
 //             outputs in the decode waves' accumulator order
 //   part_lse  fp32 [num_parts + B][H]
 // A partial computed by workgroup w for sequence b lives in slot w + b.
@@ -61,7 +61,7 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int32_t* plan;
-  float* part_o;
+  uint16_t* part_o;
   float* part_lse;
   uint16_t* o_lat;
   float* lse;

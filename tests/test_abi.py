@@ -53,9 +53,10 @@ def test_cache_bytes_per_token():
 def test_workspace_size():
     d = mla.make_dims(128, 512, 64, 128, 128, 64)
     n = lib.mla_decode_workspace_size(ctypes.byref(d), 64, 256)
-    # plan (66 int32) + partial O and lse for 256 + 64 slots, 256-byte aligned pieces
-    assert n >= (256 + 64) * 128 * (512 + 1) * 4
-    assert n < (256 + 64) * 128 * (512 + 1) * 4 + 4096
+    # plan (66 int32) + partial O (bf16) and lse (fp32) for 256 + 64 slots,
+    # 256-byte aligned pieces
+    assert n >= (256 + 64) * 128 * (512 * 2 + 4)
+    assert n < (256 + 64) * 128 * (512 * 2 + 4) + 4096
     assert lib.mla_decode_workspace_size(ctypes.byref(d), 0, 256) == 0
     bad = mla.make_dims(128, 256, 64, 128, 128, 64)
     assert lib.mla_decode_workspace_size(ctypes.byref(bad), 4, 8) == 0
