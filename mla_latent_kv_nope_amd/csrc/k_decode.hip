@@ -163,27 +163,31 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* seq_lens, int B, i
 template <int DC, int DR, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu((NW + 3) / 4, (NW + 3) / 4)))
-void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
-             const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table) {
+void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __restrict__ seq_lens,
+             const int32_t* __restrict__ block_table) {
   using Cfg = DecodeCfg<DC, DR, NW>;
   constexpr int R = Cfg::R, ROWB = Cfg::ROWB, CPR = Cfg::CPR;
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES];
-  __shared__ int redo;
+  constexpr int CPW = Cfg::VCB / NW;          // PV column blocks per wave
+  constexpr int PROW = 2 * kTile;             // bytes of one head's P row (bf16 per token)
+  constexpr int PSLOT = 16 * NW * PROW;       // P of one tile, all heads
+  static_assert(Cfg::VCB % NW == 0, "column blocks split evenly over the waves");
+  static_assert(PROW == 64, "P rows are four 16-byte chunks");
+  static_assert(!Cfg::BLOCKED || CPW % 4 == 0, "blocked PV reads start at a multiple of 4 column blocks");
+  // tile ring, then two P slots (the second also carries the per-head 1/l at
+  // the end of a piece; the first the overflow vote)
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES + 2 * PSLOT];
+  char* const pbuf = lds + Cfg::NBUF * Cfg::TILE_BYTES;
+  int* const vote = reinterpret_cast<int*>(pbuf);
+  float* const inv_share = reinterpret_cast<float*>(pbuf + PSLOT);
 
-  // workgroup -> (part, head group); the head groups of one part are 8 ids apart,
-  // which places them on the same XCD (ids are dealt round-robin to the 8 XCDs)
-  // so the second reader of a tile finds it in that XCD's L2.
-  const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
-  const int hg = y % head_groups;
-  const int w = (y / head_groups) * 8 + xcd;
+  const int w = blockIdx.x;
 
   // plan, seq_lens and block_table are read with scalar loads (restrict lets
   // the compiler prove nothing here writes them); scalar loads wait on their
   // own counter, so they never force a wait for the in-flight tile loads.
   const int B = a.B, H = a.H;
-  const int HG16 = (H + 15) >> 4;                  // 16-head groups (partial O layout)
+  const int HB = (H + 15) >> 4;               // 16-head blocks
   const int cap = a.max_pages << a.page_size_log2;
-
 
   const int total = plan[B];
   const int quota = plan[B + 1];
@@ -197,7 +201,9 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
   const int l16 = lane & 15;
   const int lg = a.page_size_log2;
   const int ps = 1 << lg;
-  const int hbase = (hg * NW + wave) * 16;   // first head of this wave
+  const int hbase = wave * 16;         // QK: first head of this wave
+  const bool qk_wave = hbase < H;
+  const int cb0 = wave * CPW;          // PV: first column block of this wave
   constexpr int REM = Cfg::INSTR % NW;
   const bool hi_loader = REM == 0 || wave < REM;
 
@@ -245,6 +251,14 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
     const int trr = (l & 15) >> 2, trq = l & 3;
     return lds_off<Cfg>(4 * (l >> 4) + trr, trq >> 1) + (trq & 1) * 8;
   };
+  // P slots: row h (one head, 64 bytes) holds the head's P in PV k-slot order;
+  // 16-byte chunk q (k slots 8q..8q+7) sits at chunk q ^ ((h >> 2) & 3), so the
+  // 16 rows read or written by a 16-lane group fall in distinct banks.
+  auto p_lane_off = [&]() -> uint32_t {
+    const int l = lane_id_fresh();
+    const int r = l & 15;
+    return static_cast<uint32_t>(r * PROW + (((l >> 4) ^ (r >> 2)) & 3) * 16);
+  };
   // Tile loads (blocked): lane l of every 1 KB load fills row l/8 of its block
   // with logical chunk (l%8) ^ (l/8); the per-lane source offset is the same for
   // every block.  Recomputed per tile (see lane_id_fresh) to keep registers free.
@@ -266,10 +280,19 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
     const char* pool = static_cast<const char*>(a.pool);
     const int64_t page_bytes = static_cast<int64_t>(ROWB) << lg;
 
+    // Page ids of the piece's first 64 pages, one per lane, loaded once per
+    // piece: the tile loop reads them with v_readlane instead of a scalar
+    // memory load (whose latency would stall every tile issue).
+    const int pfirst = (lt0 * kTile) >> lg;
+    const int pg_lane = pfirst + lane < a.max_pages ? bt[pfirst + lane] : -1;
+    auto page_id = [&](int tok) -> int {
+      const int rel = (tok >> lg) - pfirst;      // uniform
+      return rel < 64 ? __builtin_amdgcn_readlane(pg_lane, rel) : bt[tok >> lg];
+    };
     // Rows past the sequence (or on a page id outside the pool) load the same
     // chunk of the tile's first row instead, which is always a valid token.
     auto page_base = [&](int tok) -> const char* {
-      const int pg = bt[tok >> lg];
+      const int pg = page_id(tok);
       return (pg >= 0 && pg < a.num_pages) ? pool + pg * page_bytes + (tok & (ps - 1)) * ROWB
                                            : nullptr;
     };
@@ -301,10 +324,7 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
             const bool ok = rb != nullptr && row0 != nullptr && tok0 + t < S;
             src = ok ? rb + ((ps >= kTile || t < 16) ? t : t - 16) * ROWB + c * 16 : fb + c * 16;
           }
-          __builtin_amdgcn_global_load_lds(
-              reinterpret_cast<const void*>(src),
-              reinterpret_cast<lds_void_t*>(reinterpret_cast<uintptr_t>(dst_tile + blk * 1024)),
-              16, 0, 0);
+          lds_dma16_v(src, lds_addr(dst_tile + blk * 1024));
         }
       }
     };
@@ -316,7 +336,7 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
         // contiguous run; every load is (scalar block base) + (the lane's fixed
         // offset), with nothing to select per lane.
         if (ps >= kTile && tok0 + kTile <= S) {
-          const int pg = bt[tok0 >> lg];
+          const int pg = page_id(tok0);
           if (pg >= 0 && pg < a.num_pages) {
             const char* tile0 = pool + pg * page_bytes + (tok0 & (ps - 1)) * ROWB;
             const uint32_t ld_off = ld_lane().off;
@@ -325,11 +345,7 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
               const int blk = k * NW + wave;
               if (blk < Cfg::INSTR) {
                 const int bi = blk / Cfg::CG, bj = blk - bi * Cfg::CG;
-                const char* blk_base = tile0 + (8 * bi * ROWB + bj * 128);
-                __builtin_amdgcn_global_load_lds(
-                    reinterpret_cast<const void*>(blk_base + ld_off),
-                    reinterpret_cast<lds_void_t*>(reinterpret_cast<uintptr_t>(dst_tile + blk * 1024)),
-                    16, 0, 0);
+                lds_dma16(tile0 + (8 * bi * ROWB + bj * 128), ld_off, lds_addr(dst_tile + blk * 1024));
               }
             }
             return;
@@ -339,7 +355,8 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
       issue_general(tok0, dst_tile);
     };
 
-    // query registers: lane holds head hbase + l16, elements [32kc + 8*quad, +8)
+    // query registers (QK waves): lane holds head hbase + l16, elements
+    // [32kc + 8*quad, +8)
     bf16x8 qreg[Cfg::K32];
     bf16x8 qtail = {};  // elements [32*K32 + 8*quad, +8) for quad < 2, zero otherwise
     {
@@ -359,20 +376,26 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
       }
     }
 
-    f32x4 o[Cfg::VCB];
+    // O of this wave: heads 16hb + 4quad + i (all heads), columns
+    // 16(cb0 + c) + l16
+    f32x4 o[NW][CPW];
     float m_use = -INFINITY;   // exponent offset for this lane's head (set by the first tile)
     float m_seen = -INFINITY;  // running maximum of this head's scores
     float l_part = 0.f;        // this lane's share of the softmax denominator
     for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int cb = 0; cb < Cfg::VCB; ++cb) o[cb] = f32x4{};
+    for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) o[hb][c] = f32x4{};
     l_part = 0.f;
     bool overflow = false;
 
-    // Software pipeline over tiles: iteration `it` computes S(it) = K(it).Q^T,
-    // then PV(it - 1) (P of the previous tile, V from its still-resident ring
-    // slot) interleaved with the softmax of S(it).  Two ring slots are read per
-    // iteration, so AHEAD = NBUF - 2 tiles are in flight.
+    // Software pipeline over tiles: iteration `it` computes S(it) = K(it).Q^T
+    // and its softmax (QK waves: 16 heads each), publishes P(it) in P slot it%2,
+    // then accumulates PV(it - 1) (every wave: all heads, its own columns; P of
+    // the previous tile, V from its still-resident ring slot).  Two ring slots
+    // are read per iteration, so AHEAD = NBUF - 2 tiles are in flight; the one
+    // barrier per tile both releases a ring slot and publishes P.
     constexpr int AHEAD = Cfg::NBUF - 2;
     static_assert(AHEAD >= 1, "ring too small");
 #pragma unroll
@@ -463,35 +486,54 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
       return __builtin_bit_cast(bf16x8, pu);
     };
 
-    // ---- O += P . V_tile.  Transpose-read source lane 4r+q of group `quad`
-    // reads token rows 4*quad + r and 16 + 4*quad + r at channels 16cb + 4q;
-    // the swizzled address is one of four bases (by cb % 4) plus immediates.
-    // B operands are read PD MFMAs ahead; the scheduler may interleave the
-    // independent softmax VALU work of the next tile between these MFMAs.
-    auto pv = [&](const char* tb, bf16x8 pa) {
-      constexpr int PD = Cfg::VCB < kPvAhead ? Cfg::VCB : kPvAhead;
+    auto p_store = [&](int pslot, bf16x8 pa) {
+      *reinterpret_cast<bf16x8*>(pbuf + pslot * PSLOT + hbase * PROW + p_lane_off()) = pa;
+    };
+
+    // ---- O += P . V_tile over all head blocks and this wave's CPW column
+    // blocks.  B (V, transpose reads: source lane 4r+q of group `quad` reads
+    // token rows 4*quad + r and 16 + 4*quad + r at channels 16cb + 4q) is held
+    // for CG column blocks while the head blocks' A operands (P rows, one
+    // 16-byte read each) stream past.
+    auto pv = [&](const char* tb, int pslot) {
       // tile buffers are 4 KB aligned, so the xor may be applied after adding
       // the buffer address
-      const uintptr_t pb = reinterpret_cast<uintptr_t>(tb) + pv_base0();
-      auto v_read = [&](int cb) {
-        const int imm = Cfg::BLOCKED ? 1024 * (cb >> 2) : 32 * cb;
-        const char* p0 = reinterpret_cast<const char*>(
-                             Cfg::BLOCKED ? (pb ^ static_cast<uintptr_t>(32 * (cb & 3))) : pb) + imm;
+      // (blocked: cb0 is a multiple of 4, so the wave's first column block
+      // only moves the base by whole 1 KB blocks, which the xor leaves alone)
+      const uint32_t pb = pv_base0() + (Cfg::BLOCKED ? 1024 * (cb0 >> 2) : 32 * cb0);
+      auto v_read = [&](int c) {                  // column block cb0 + c
+        const int imm = Cfg::BLOCKED ? 1024 * (c >> 2) : 32 * c;
+        const char* p0 = tb + (Cfg::BLOCKED ? (pb ^ static_cast<uint32_t>(32 * (c & 3))) : pb) + imm;
         const bf16x4 v0 = lds_read_tr16(p0);
         const bf16x4 v1 = lds_read_tr16(p0 + 16 * ROWB);
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      bf16x8 vbuf[PD];
+      const char* pa_base = pbuf + pslot * PSLOT + p_lane_off();
+      constexpr int CG = CPW < 4 ? CPW : 4;
 #pragma unroll
-      for (int i = 0; i < PD; ++i) vbuf[i] = v_read(i);
+      for (int c0 = 0; c0 < CPW; c0 += CG) {
+        bf16x8 vb[CG];
 #pragma unroll
-      for (int cb = 0; cb < Cfg::VCB; ++cb) {
-        o[cb] = mfma16(pa, vbuf[cb % PD], o[cb]);
-        if (cb + PD < Cfg::VCB) vbuf[cb % PD] = v_read(cb + PD);
+        for (int c = 0; c < CG; ++c) vb[c] = v_read(c0 + c);
+        // every head block, also those past H (never stored): no branches, so
+        // the A reads can run AD head blocks ahead
+        constexpr int AD = NW < 3 ? NW : 3;
+        bf16x8 abuf[AD];
+#pragma unroll
+        for (int i = 0; i < AD; ++i) abuf[i] = *reinterpret_cast<const bf16x8*>(pa_base + i * 16 * PROW);
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb) {
+          const bf16x8 pa = abuf[hb % AD];
+          if (hb + AD < NW) abuf[hb % AD] = *reinterpret_cast<const bf16x8*>(pa_base + (hb + AD) * 16 * PROW);
+#pragma unroll
+          for (int c = 0; c < CG; ++c) o[hb][c0 + c] = mfma16(pa, vb[c], o[hb][c0 + c]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      sched_interleave<Cfg::VCB, 2, PD>();
     };
 
+    // waits for tile it, then issues the loads of tile it + AHEAD into the
+    // ring slot the barrier just released
     auto wait_and_sync = [&](int it) {
       const int pending = min(ntiles - 1 - it, AHEAD - 1);
       if (hi_loader) wait_tiles<AHEAD + 2, Cfg::LD_HI>(pending);
@@ -500,91 +542,114 @@ void k_split(DecodeArgs a, int head_groups, const int32_t* __restrict__ plan,
       if (it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
     };
 
-    f32x4 sacc[2];
-    bf16x8 pa;
-    // first tile: QK + softmax (sets the exponent offset on the first pass)
+    // QK + softmax of one tile, P published to its slot (QK waves only)
+    auto score_tile = [&](const char* tb, int tok0, bool set_offset, int pslot) {
+      if (qk_wave) {
+        f32x4 sacc[2];
+        qk(tb, sacc);
+        p_store(pslot, softmax(sacc, tok0, set_offset));
+      }
+    };
+
+    // first tile: QK + softmax (sets the exponent offset on the first pass);
+    // then each step computes S(it), its softmax and P(it), and PV(it - 1)
     wait_and_sync(0);
-    qk(lds, sacc);
-    pa = softmax(sacc, lt0 * kTile, pass == 0);
+    score_tile(lds, lt0 * kTile, pass == 0, 0);
     for (int it = 1; it < ntiles; ++it) {
       wait_and_sync(it);
-      const char* tb = lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES;
-      qk(tb, sacc);
-      const bf16x8 pa_prev = pa;
-      pv(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, pa_prev);
-      pa = softmax(sacc, (lt0 + it) * kTile, false);
+      score_tile(lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES, (lt0 + it) * kTile, false, it & 1);
+      pv(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (it - 1) & 1);
     }
     // last tile's PV (its ring slot is not refilled: no later loads)
-    pv(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, pa);
+    block_barrier();
+    pv(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1);
 
     // a score far above the offset anywhere in the workgroup: redo the piece
     // with each head's true maximum as its offset (cannot overflow again)
-    if (threadIdx.x == 0) redo = 0;
+    __syncthreads();                 // P slots are free from here on
+    if (threadIdx.x == 0) *vote = 0;
     __syncthreads();
-    if (__builtin_amdgcn_ballot_w64(overflow) != 0 && lane == 0) redo = 1;
+    if (__builtin_amdgcn_ballot_w64(overflow) != 0 && lane == 0) *vote = 1;
     __syncthreads();
-    const bool again = redo != 0;
+    const bool again = *vote != 0;
     __syncthreads();
     if (!again || pass > 0) break;   // the second pass starts at the true maximum
     m_use = m_seen;
     }  // pass
 
-    // ---- epilogue: normalise and write
+    // ---- epilogue: the QK waves publish 1/l of their heads and write the lse;
+    // every wave normalises and writes its columns of O
     const float l_tot = sum_across_half_waves(sum_across_quarter_pairs(l_part));
-    const float inv = 1.0f / l_tot;
     const float lse_nat = (m_use + log2f(l_tot)) * kLn2;
-    // this lane's 4 heads (4*quad + i) scaled by 1 / l
-    f32x4 scv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) scv[i] = shfl_f32(inv, 4 * quad + i);
-#pragma unroll
-    for (int cb = 0; cb < Cfg::VCB; ++cb) o[cb] *= scv;
-
-    // o_lat rows of this wave's 16 heads: lane (quad, l16) writes channel
-    // 16cb + l16 of heads 4quad + i at an immediate offset from one of four
-    // lane offsets; heads past H get an offset beyond the buffer's range, whose
-    // stores the hardware drops
-    // (Lane-derived values of the epilogue are recomputed from lane_id_fresh so
-    // that none of them is hoisted into a register held across the tile loop.)
-    auto store_olat = [&]() {
-      const auto rs = make_rsrc(a.o_lat + (static_cast<int64_t>(b) * H + hbase) * DC, 16 * DC * 2);
-      const int fl = lane_id_fresh();
-      const int fq = fl >> 4, f16 = fl & 15;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t vo = hbase + 4 * fq + i < H
-                                ? static_cast<uint32_t>((4 * fq + i) * DC + f16) * 2 : 0x80000000u;
-#pragma unroll
-        for (int cb = 0; cb < Cfg::VCB; ++cb)
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(o[cb][i])), rs, vo,
-                                                32 * cb, 0);
+    const int64_t slot = static_cast<int64_t>(w) + b;
+    if (qk_wave && quad == 0) {
+      inv_share[hbase + l16] = 1.0f / l_tot;
+      if (hbase + l16 < H) {
+        if (whole) {
+          if (a.lse != nullptr) a.lse[static_cast<int64_t>(b) * H + hbase + l16] = lse_nat;
+        } else {
+          a.part_lse[slot * H + hbase + l16] = lse_nat;
+        }
       }
-    };
+    }
+    __syncthreads();
+    // (lane-derived values below come from lane_id_fresh so that none of them
+    // is hoisted into a register held across the tile loop)
+    const int fl = lane_id_fresh();
+    const int fq = fl >> 4, f16 = fl & 15;
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      if (hb < HB) {
+        f32x4 scv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) scv[i] = inv_share[hb * 16 + 4 * fq + i];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) o[hb][c] *= scv;
+      }
+    }
 
     if (whole) {
-      store_olat();
-      if (a.lse != nullptr && quad == 0 && hbase + l16 < H)
-        a.lse[static_cast<int64_t>(b) * H + hbase + l16] = lse_nat;
-    } else {
-      // Partial piece: normalised O rounded to bf16 in this wave's accumulator
-      // order, one 8-byte store per lane and column block, and its lse (fp32);
-      // k_combine merges them.
-      const int64_t slot = static_cast<int64_t>(w) + b;
-      if (hbase < H) {   // waves past the last head have nothing to store
-        constexpr uint32_t kPieceBytes = Cfg::VCB * 64 * 8;    // 16 heads x d_c bf16
-        const auto rs = make_rsrc(a.part_o + (slot * HG16 + (hbase >> 4)) * (kPieceBytes / 2), kPieceBytes);
-        const uint32_t voff = static_cast<uint32_t>(lane_id_fresh()) * 8;
+      // o_lat[b]: lane (quad, l16) writes column 16(cb0 + c) + l16 of heads
+      // 16hb + 4quad + i; heads past H get an offset beyond the buffer's
+      // range, whose stores the hardware drops
+      const auto rs = make_rsrc(a.o_lat + static_cast<int64_t>(b) * H * DC, H * DC * 2);
 #pragma unroll
-        for (int cb = 0; cb < Cfg::VCB; ++cb) buffer_store_bf16x4(o[cb], rs, voff, cb * 512);
+      for (int hb = 0; hb < NW; ++hb) {
+        if (hb < HB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int h = hb * 16 + 4 * fq + i;
+            const uint32_t vo = h < H ? static_cast<uint32_t>(h * DC + 16 * cb0 + f16) * 2 : 0x80000000u;
+#pragma unroll
+            for (int c = 0; c < CPW; ++c)
+              __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(o[hb][c][i])), rs,
+                                                    vo, 32 * c, 0);
+          }
+        }
       }
-      if (quad == 0 && hbase + l16 < H) a.part_lse[slot * H + hbase + l16] = lse_nat;
+    } else {
+      // Partial piece: normalised O rounded to bf16 in accumulator order
+      // ([head block][column block][lane][4]), one 8-byte store per lane and
+      // block; k_combine merges the pieces.
+      constexpr uint32_t kBlk = 64 * 8;                        // one 16 x 16 block, bf16
+      const auto rs = make_rsrc(a.part_o + slot * HB * Cfg::VCB * (kBlk / 2), HB * Cfg::VCB * kBlk);
+      const uint32_t voff = static_cast<uint32_t>(fl) * 8;
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb) {
+        if (hb < HB) {
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+            buffer_store_bf16x4(o[hb][c], rs, voff, (hb * Cfg::VCB + cb0 + c) * kBlk);
+        }
+      }
     }
 
     // next piece: the next non-empty sequence
     g = t0 + lt1;
     ++b;
     while (b < B && plan[b + 1] <= g) ++b;
-    // all waves must be done reading the ring before the next piece refills it
+    // all waves must be done reading the ring and the shared 1/l before the
+    // next piece refills them
     __syncthreads();
   }
 }
@@ -708,9 +773,7 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
 
 template <int DC, int DR, int NW>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
-  const int hg = (a.H + 16 * NW - 1) / (16 * NW);
-  const int parts8 = (a.num_parts + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_split<DC, DR, NW>), dim3(parts8 * hg), dim3(64 * NW), 0, s, a, hg,
+  hipLaunchKernelGGL((k_split<DC, DR, NW>), dim3(a.num_parts), dim3(64 * NW), 0, s, a,
                      static_cast<const int32_t*>(a.plan), a.seq_lens, a.block_table);
   return hipGetLastError();
 }
@@ -757,13 +820,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
-#ifndef MLA_DECODE_WAVES
-#define MLA_DECODE_WAVES 8
-#endif
   if (a.d_c == 512 && a.d_rope == 64) {
     if (a.H <= 16) e = launch_split<512, 64, 1>(a, s);
     else if (a.H <= 32) e = launch_split<512, 64, 2>(a, s);
-    else e = launch_split<512, 64, MLA_DECODE_WAVES>(a, s);
+    else e = launch_split<512, 64, 8>(a, s);
   } else if (a.d_c == 32 && a.d_rope == 16) {
     if (a.H <= 16) e = launch_split<32, 16, 1>(a, s);
     else e = launch_split<32, 16, 2>(a, s);

@@ -53,9 +53,13 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // the 8 bytes read by source lane 4*e + i/4, for e = 0..3.  With source lane
 // 4r+q pointing at row r, columns [4q, 4q+4) of a row-major 16-bit tile, lane i
 // receives column i of rows 0..3.
+// The pointer must point into a __shared__ array; it is converted with an
+// address-space cast (not through an integer), so the compiler still knows
+// which object is read: a read whose object is unknown makes it wait for every
+// in-flight global->LDS copy first.
 __device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds_ptr) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(lds_ptr)));
+      (__attribute__((address_space(3))) i16x4*)(const_cast<void*>(lds_ptr)));
   return __builtin_bit_cast(bf16x4, v);
 }
 
@@ -89,6 +93,38 @@ __device__ __forceinline__ f32x4 buffer_load_bf16x4(__amdgpu_buffer_rsrc_t r, ui
   const uint32_t lo = static_cast<uint32_t>(p[0]), hi = static_cast<uint32_t>(p[1]);
   return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u), __uint_as_float(hi << 16),
                __uint_as_float(hi & 0xffff0000u)};
+}
+
+// ---- global -> LDS copies -------------------------------------------------
+// 16 bytes per lane from global memory straight into LDS: lane l writes LDS
+// bytes [lds + 16l, +16).  Issued through inline assembly so that the
+// compiler does not track them: it would otherwise make transpose reads wait
+// for every copy in flight.  The caller orders them with wait_vmcnt and a
+// workgroup barrier before the data is read.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+// (wave-uniform operands are passed through readfirstlane so that they are
+// scalar registers)
+__device__ __forceinline__ uint64_t uniform_u64(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+// source = sbase (wave-uniform) + voff (per lane)
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  __asm__ __volatile__("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                       :
+                       : "v"(voff), "s"(uniform_u64(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                       : "memory", "m0");
+}
+// source = per-lane address
+__device__ __forceinline__ void lds_dma16_v(const void* src, uint32_t lds) {
+  __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                       :
+                       : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+                       : "memory", "m0");
 }
 
 // ---- waits and barriers ---------------------------------------------------
