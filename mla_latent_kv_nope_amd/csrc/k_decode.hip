@@ -55,6 +55,9 @@ constexpr float kHeadroom = 64.0f;  // log2 units
 #ifndef MLA_PV_AHEAD
 #define MLA_PV_AHEAD 3
 #endif
+#ifndef MLA_LOADER_WAVES
+#define MLA_LOADER_WAVES 0
+#endif
 constexpr int kQkAhead = MLA_QK_AHEAD;
 constexpr int kPvAhead = MLA_PV_AHEAD;
 
@@ -71,8 +74,11 @@ struct DecodeCfg {
   static constexpr int TILE_BYTES = kTile * ROWB;
   static constexpr int INSTR = kTile * CPR / 64;     // 1 KB wave loads per tile
   static constexpr int THREADS = 64 * NW;
-  static constexpr int LD_HI = (INSTR + NW - 1) / NW;  // loads of waves < INSTR % NW (or all)
-  static constexpr int LD_LO = INSTR / NW;
+  // tile loads are issued by the last LW waves (the others start computing
+  // right after each barrier); loader i issues blocks i, i + LW, ...
+  static constexpr int LW = (MLA_LOADER_WAVES > 0 && MLA_LOADER_WAVES < NW) ? MLA_LOADER_WAVES : NW;
+  static constexpr int LD_HI = (INSTR + LW - 1) / LW;  // loads of loaders < INSTR % LW (or all)
+  static constexpr int LD_LO = INSTR / LW;
   static constexpr int K32 = R / 32;                 // full 32-wide QK chunks
   static constexpr bool K16 = (R % 32) == 16;        // one 16-wide tail chunk
   static constexpr int VCB = DC / 16;                // PV column blocks
@@ -204,8 +210,10 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
   const int hbase = wave * 16;         // QK: first head of this wave
   const bool qk_wave = hbase < H;
   const int cb0 = wave * CPW;          // PV: first column block of this wave
-  constexpr int REM = Cfg::INSTR % NW;
-  const bool hi_loader = REM == 0 || wave < REM;
+  constexpr int REM = Cfg::INSTR % Cfg::LW;
+  const int loader = wave - (NW - Cfg::LW);      // loader index, negative for non-loaders
+  const bool hi_loader = loader >= 0 && (REM == 0 || loader < REM);
+  const bool lo_loader = loader >= 0 && !hi_loader;
 
   // rows that are skipped keep whatever the buffer held; start from zeros so it is finite
   for (int i = threadIdx.x; i < Cfg::NBUF * Cfg::TILE_BYTES / 16; i += Cfg::THREADS)
@@ -304,8 +312,8 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
       const char* fb = row0 ? row0 : pool;
 #pragma unroll
       for (int k = 0; k < Cfg::LD_HI; ++k) {
-        const int blk = k * NW + wave;               // 1 KB block of the tile this load fills
-        if (blk < Cfg::INSTR) {
+        const int blk = k * Cfg::LW + loader;        // 1 KB block of the tile this load fills
+        if (loader >= 0 && blk < Cfg::INSTR) {
           const char* src;
           if constexpr (Cfg::BLOCKED) {
             const int bi = blk / Cfg::CG, bj = blk - bi * Cfg::CG;
@@ -342,8 +350,8 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
             const uint32_t ld_off = ld_lane().off;
 #pragma unroll
             for (int k = 0; k < Cfg::LD_HI; ++k) {
-              const int blk = k * NW + wave;
-              if (blk < Cfg::INSTR) {
+              const int blk = k * Cfg::LW + loader;
+              if (loader >= 0 && blk < Cfg::INSTR) {
                 const int bi = blk / Cfg::CG, bj = blk - bi * Cfg::CG;
                 lds_dma16(tile0 + (8 * bi * ROWB + bj * 128), ld_off, lds_addr(dst_tile + blk * 1024));
               }
@@ -534,12 +542,21 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
 
     // waits for tile it, then issues the loads of tile it + AHEAD into the
     // ring slot the barrier just released
+    // The waves of the first half get the matrix core first on their SIMD and
+    // would idle at the next barrier; they issue their share of the loads at
+    // the end of the step instead (the slot is free from this step's barrier
+    // on), while the second half issues right after the barrier.
+    const bool late_issue = wave < NW / 2;
     auto wait_and_sync = [&](int it) {
       const int pending = min(ntiles - 1 - it, AHEAD - 1);
       if (hi_loader) wait_tiles<AHEAD + 2, Cfg::LD_HI>(pending);
-      else wait_tiles<AHEAD + 2, Cfg::LD_LO>(pending);
+      else if (lo_loader) wait_tiles<AHEAD + 2, Cfg::LD_LO>(pending);
+      else wait_vmcnt<0>();
       block_barrier();
-      if (it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
+      if (!late_issue && it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
+    };
+    auto late = [&](int it) {
+      if (late_issue && it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
     };
 
     // QK + softmax of one tile, P published to its slot (QK waves only)
@@ -555,10 +572,12 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
     // then each step computes S(it), its softmax and P(it), and PV(it - 1)
     wait_and_sync(0);
     score_tile(lds, lt0 * kTile, pass == 0, 0);
+    late(0);
     for (int it = 1; it < ntiles; ++it) {
       wait_and_sync(it);
       score_tile(lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES, (lt0 + it) * kTile, false, it & 1);
       pv(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (it - 1) & 1);
+      late(it);
     }
     // last tile's PV (its ring slot is not refilled: no later loads)
     block_barrier();
