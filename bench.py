@@ -41,7 +41,47 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=24,
                     help="sequences of the workload the oracle decodes for cpu_baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run three device-to-device copies of MIB MiB (a kernel of known "
+                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per k_split launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when the kernel sources changed since it was taken or
+    the workload differs."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "k_split_v3_b64_s8192.md")
+    try:
+        text = open(path, encoding="utf-8").read()
+        block = json.loads(re.search(r"```json\n(.*?)```", text, re.S).group(1))
+    except (OSError, AttributeError, ValueError):
+        return None
+    if block.get("workload") != workload:
+        return None
+    for rel, digest in block["sources_sha256"].items():
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
+    return int(block["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(inp, n_seq: int):
@@ -64,6 +104,9 @@ def cpu_baseline(inp, n_seq: int):
 
 def main():
     args = parse()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; the decode path shards by sequence "
               "(attention data parallel) and needs no collective, but multi-GPU runs are not "
@@ -142,7 +185,8 @@ def main():
     bound = "mfma" if wl.fp8 else "hbm"
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.workload)}
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
