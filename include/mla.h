@@ -166,6 +166,9 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t B, int32_t num_
  * with s_t = softmax_scale * (q[b][h] . row_t) over t < seq_lens[b] and
  * p = softmax(s).  A sequence of length 0 yields o_lat = 0 and lse = -inf.
  * Results differ between split counts only by floating-point rounding.
+ * fp8 cache (d_c = 512, d_rope = 64 only, else MLA_ERR_UNSUPPORTED): row_t is
+ * the dequantised row code * scale[t] (zskr.cn section 5, mixed-precision
+ * FP8 cache; fsdata.site section 3.1), rounded to bf16 before the products.
  */
 mla_status_t mla_decode_paged(const mla_dims_t* dims, const void* q, const void* pool,
                               const float* scales, const int32_t* block_table, int32_t max_pages,

@@ -61,7 +61,7 @@ constexpr float kHeadroom = 64.0f;  // log2 units
 constexpr int kQkAhead = MLA_QK_AHEAD;
 constexpr int kPvAhead = MLA_PV_AHEAD;
 
-template <int DC, int DR, int NW>
+template <int DC, int DR, int NW, bool FP8 = false>
 struct DecodeCfg {
   static constexpr int R = DC + DR;
   static constexpr int ROWB = 2 * R;                 // bytes per bf16 row
@@ -88,7 +88,19 @@ struct DecodeCfg {
     while ((n + 1) * TILE_BYTES <= LDS_MAX && (n - 1) * LD_HI <= 63 && n < 4) ++n;
     return n;
   }
-  static constexpr int NBUF = nbuf();
+  // fp8 cache: the bf16 ring keeps the two tiles in use (QK and PV); fp8 tiles
+  // (+ their 32 per-token scales) stream into a ring of SNB staging slots and
+  // are converted to bf16 between two barriers
+  static constexpr int NBUF = FP8 ? 2 : nbuf();
+  static constexpr int F8_TILE = kTile * R;             // bytes of an fp8 tile
+  static constexpr int F8_BLK = (F8_TILE + 1023) / 1024;
+  static constexpr int F8_SLOT = F8_TILE + 4 * kTile;   // + fp32 scales
+  static constexpr int SNB = 3;
+  static constexpr int STAGE_BYTES = FP8 ? SNB * F8_SLOT : 0;
+  static_assert(!FP8 || (BLOCKED && F8_TILE % 1024 == 0 && F8_SLOT % 128 == 0), "fp8 tile shape");
+  // rows of a tile in one 1 KB copy block never straddle the 16-row boundary
+  // (a tile spans two pages when pages hold 16 tokens)
+  static_assert(!FP8 || (16 * R) % 1024 == 0, "fp8 half tiles are whole copy blocks");
   static_assert(R % 16 == 0 && DC % 16 == 0, "dims");
   static_assert((kTile * CPR) % 64 == 0, "tile load split");
   static_assert((NBUF - 2) * LD_HI <= 63, "vmcnt range");
@@ -115,6 +127,18 @@ __device__ __forceinline__ void wait_tiles(int pending) {
     if (pending >= 1) { wait_vmcnt<L>(); return; }
   }
   wait_vmcnt<0>();
+}
+
+// waits until at most n (0 <= n, clamped to N) vector memory operations of
+// this wave are outstanding; n is wave-uniform
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) wait_vmcnt<N>();
+    else wait_vmcnt_le<N - 1>(n);
+  }
 }
 
 // Scheduling hint for a run of N MFMAs, each fed by RD LDS reads: issue the
@@ -166,12 +190,12 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* seq_lens, int B, i
 }
 
 // ---------------------------------------------------------------------------
-template <int DC, int DR, int NW>
+template <int DC, int DR, int NW, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu((NW + 3) / 4, (NW + 3) / 4)))
 void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __restrict__ seq_lens,
              const int32_t* __restrict__ block_table) {
-  using Cfg = DecodeCfg<DC, DR, NW>;
+  using Cfg = DecodeCfg<DC, DR, NW, FP8>;
   constexpr int R = Cfg::R, ROWB = Cfg::ROWB, CPR = Cfg::CPR;
   constexpr int CPW = Cfg::VCB / NW;          // PV column blocks per wave
   constexpr int PROW = 2 * kTile;             // bytes of one head's P row (bf16 per token)
@@ -179,10 +203,11 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
   static_assert(Cfg::VCB % NW == 0, "column blocks split evenly over the waves");
   static_assert(PROW == 64, "P rows are four 16-byte chunks");
   static_assert(!Cfg::BLOCKED || CPW % 4 == 0, "blocked PV reads start at a multiple of 4 column blocks");
-  // tile ring, then two P slots (the second also carries the per-head 1/l at
-  // the end of a piece; the first the overflow vote)
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES + 2 * PSLOT];
-  char* const pbuf = lds + Cfg::NBUF * Cfg::TILE_BYTES;
+  // tile ring, (fp8: staging slots,) then two P slots (the second also
+  // carries the per-head 1/l at the end of a piece; the first the overflow vote)
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES + Cfg::STAGE_BYTES + 2 * PSLOT];
+  char* const stage = lds + Cfg::NBUF * Cfg::TILE_BYTES;
+  char* const pbuf = stage + Cfg::STAGE_BYTES;
   int* const vote = reinterpret_cast<int*>(pbuf);
   float* const inv_share = reinterpret_cast<float*>(pbuf + PSLOT);
 
@@ -363,6 +388,66 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
       issue_general(tok0, dst_tile);
     };
 
+    // ---- fp8 cache.  Copies of one tile (R bytes per token) and its 32
+    // per-token scales into a staging slot.  Per lane: 16 bytes of row r; rows
+    // past the sequence, or on a page outside the pool, copy the tile's first
+    // row instead (and its scale), so converted rows are always finite.  A
+    // 1 KB copy block lies in one 16-row half of the tile, hence in one page.
+    const uint8_t* const pool8 = static_cast<const uint8_t*>(a.pool);
+    const int64_t page_bytes8 = static_cast<int64_t>(R) << lg;
+    auto issue_tile8 = [&](int lt, int sslot) {
+      const int tok0 = lt * kTile;
+      char* dst = stage + sslot * Cfg::F8_SLOT;
+      const int pg0 = page_id(tok0);
+      const int pg1 = ps >= kTile ? pg0 : page_id(tok0 + 16);
+      const bool ok0 = pg0 >= 0 && pg0 < a.num_pages;
+      const bool ok1 = pg1 >= 0 && pg1 < a.num_pages;
+      const uint8_t* row0 = ok0 ? pool8 + pg0 * page_bytes8 + (tok0 & (ps - 1)) * R : pool8;
+      const int l = lane_id_fresh();
+#pragma unroll
+      for (int j = 0; j < (Cfg::F8_BLK + NW - 1) / NW; ++j) {
+        const int blk = j * NW + wave;
+        if (blk < Cfg::F8_BLK) {
+          const int b = blk * 1024 + 16 * l;
+          const int r = b / R, c = b - r * R;
+          const bool hi = r >= 16;
+          const int pg = hi ? pg1 : pg0;
+          const bool ok = (hi ? ok1 : ok0) && ok0 && tok0 + r < S;
+          const uint8_t* src = ok ? pool8 + pg * page_bytes8 + ((tok0 + r) & (ps - 1)) * R + c : row0 + c;
+          lds_dma16_v(src, lds_addr(dst + blk * 1024));
+        }
+      }
+      if (wave == NW - 1 && l < kTile / 4) {       // scales of tokens 4l .. 4l + 3
+        const float* sc = a.scales;
+        const bool hi = 4 * l >= 16;
+        const int pg = hi ? pg1 : pg0;
+        const bool ok = (hi ? ok1 : ok0) && ok0 && tok0 + 4 * l < S;
+        const float* src = ok ? sc + static_cast<int64_t>(pg) * ps + ((tok0 + 4 * l) & (ps - 1))
+                              : (ok0 ? sc + static_cast<int64_t>(pg0) * ps + (tok0 & (ps - 1)) : sc);
+        lds_dma16_v(src, lds_addr(dst + Cfg::F8_TILE));
+      }
+    };
+    // vector memory operations one wave issues per fp8 tile
+    const int ld8 = (Cfg::F8_BLK - wave + NW - 1) / NW + (wave == NW - 1 ? 1 : 0);
+    // staging slot -> bf16 ring slot: 8 codes (one bf16 chunk) per unit,
+    // dequantised as code * scale and rounded to bf16 by the gfx950
+    // conversion instruction; rows past the sequence take row 0's scale
+    auto convert8 = [&](int lt, int sslot, int bslot) {
+      const int tok0 = lt * kTile;
+      const char* src = stage + sslot * Cfg::F8_SLOT;
+      const float* sls = reinterpret_cast<const float*>(src + Cfg::F8_TILE);
+      char* dst = lds + bslot * Cfg::TILE_BYTES;
+      constexpr int UPR = R / 8;                    // units per row
+      for (int u = threadIdx.x; u < kTile * UPR; u += Cfg::THREADS) {
+        const int r = u / UPR, c = u - r * UPR;
+        const uint2 x = *reinterpret_cast<const uint2*>(src + r * R + 8 * c);
+        const float scl = tok0 + r < S ? sls[r] : sls[0];
+        const uint4 y = {fp8x2_to_bf16x2<false>(x.x, scl), fp8x2_to_bf16x2<true>(x.x, scl),
+                         fp8x2_to_bf16x2<false>(x.y, scl), fp8x2_to_bf16x2<true>(x.y, scl)};
+        *reinterpret_cast<uint4*>(dst + lds_off<Cfg>(r, c)) = y;
+      }
+    };
+
     // query registers (QK waves): lane holds head hbase + l16, elements
     // [32kc + 8*quad, +8)
     bf16x8 qreg[Cfg::K32];
@@ -404,11 +489,13 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
     // the previous tile, V from its still-resident ring slot).  Two ring slots
     // are read per iteration, so AHEAD = NBUF - 2 tiles are in flight; the one
     // barrier per tile both releases a ring slot and publishes P.
-    constexpr int AHEAD = Cfg::NBUF - 2;
+    constexpr int AHEAD = FP8 ? 1 : Cfg::NBUF - 2;    // (the fp8 path stages its own tiles)
     static_assert(AHEAD >= 1, "ring too small");
+    if constexpr (!FP8) {
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i)
-      if (i < ntiles) issue_tile(lt0 + i, i);
+      for (int i = 0; i < AHEAD; ++i)
+        if (i < ntiles) issue_tile(lt0 + i, i);
+    }
 
     // ---- S^T = K_tile . Q^T.  MFMA i covers chunk kc = i/2 of token block
     // tbk = i%2 (two independent accumulator chains, interleaved).  A operand =
@@ -568,6 +655,7 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
       }
     };
 
+    if constexpr (!FP8) {
     // first tile: QK + softmax (sets the exponent offset on the first pass);
     // then each step computes S(it), its softmax and P(it), and PV(it - 1)
     wait_and_sync(0);
@@ -582,6 +670,33 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
     // last tile's PV (its ring slot is not refilled: no later loads)
     block_barrier();
     pv(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1);
+    } else {
+    // fp8: tiles it+1 .. it+SNB are in the staging ring while step it runs;
+    // step it = barrier A (bf16 tile it and P(it-1) visible, staging slot of
+    // tile it free) -> copies of tile it+SNB -> S(it), P(it) -> PV(it-1) ->
+    // wait for tile it+1 -> barrier B (bf16 slot of tile it-1 and P(it) free /
+    // visible) -> convert tile it+1 into the bf16 slot of tile it-1
+    constexpr int SNB = Cfg::SNB;
+#pragma unroll
+    for (int i = 0; i < SNB; ++i)
+      if (i < ntiles) issue_tile8(lt0 + i, i);
+    wait_vmcnt_le<2 * (Cfg::F8_BLK + 1)>(min(ntiles - 1, SNB - 1) * ld8);
+    block_barrier();
+    convert8(lt0, 0, 0);
+    for (int it = 0; it < ntiles; ++it) {
+      block_barrier();
+      if (it + SNB < ntiles) issue_tile8(lt0 + it + SNB, it % SNB);
+      score_tile(lds + (it & 1) * Cfg::TILE_BYTES, (lt0 + it) * kTile, pass == 0 && it == 0, it & 1);
+      if (it > 0) pv(lds + ((it - 1) & 1) * Cfg::TILE_BYTES, (it - 1) & 1);
+      if (it + 1 < ntiles) {
+        wait_vmcnt_le<2 * (Cfg::F8_BLK + 1)>((min(it + SNB, ntiles - 1) - (it + 1)) * ld8);
+        block_barrier();
+        convert8(lt0 + it + 1, (it + 1) % SNB, (it + 1) & 1);
+      }
+    }
+    block_barrier();
+    pv(lds + ((ntiles - 1) & 1) * Cfg::TILE_BYTES, (ntiles - 1) & 1);
+    }
 
     // a score far above the offset anywhere in the workgroup: redo the piece
     // with each head's true maximum as its offset (cannot overflow again)
@@ -790,17 +905,18 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
   }
 }
 
-template <int DC, int DR, int NW>
+template <int DC, int DR, int NW, bool FP8 = false>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_split<DC, DR, NW>), dim3(a.num_parts), dim3(64 * NW), 0, s, a,
+  hipLaunchKernelGGL((k_split<DC, DR, NW, FP8>), dim3(a.num_parts), dim3(64 * NW), 0, s, a,
                      static_cast<const int32_t*>(a.plan), a.seq_lens, a.block_table);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool decode_supported(int d_c, int d_rope, int H) {
+bool decode_supported(int d_c, int d_rope, int H, bool fp8) {
   if (H < 1 || H > 128) return false;
+  if (fp8) return d_c == 512 && d_rope == 64;
   if (d_c == 512 && d_rope == 64) return true;
   if (d_c == 32 && d_rope == 16) return H <= 32;
   return false;
@@ -839,7 +955,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
-  if (a.d_c == 512 && a.d_rope == 64) {
+  if (a.d_c == 512 && a.d_rope == 64 && a.fp8) {
+    if (a.H <= 16) e = launch_split<512, 64, 1, true>(a, s);
+    else if (a.H <= 32) e = launch_split<512, 64, 2, true>(a, s);
+    else e = launch_split<512, 64, 8, true>(a, s);
+  } else if (a.fp8) {
+    return hipErrorInvalidValue;
+  } else if (a.d_c == 512 && a.d_rope == 64) {
     if (a.H <= 16) e = launch_split<512, 64, 1>(a, s);
     else if (a.H <= 32) e = launch_split<512, 64, 2>(a, s);
     else e = launch_split<512, 64, 8>(a, s);

@@ -151,7 +151,7 @@ mla_status_t mla_absorb_q(const mla_dims_t* d, const void* q_nope, const void* q
 
 size_t mla_decode_workspace_size(const mla_dims_t* d, int32_t B, int32_t num_splits) {
   if (check_dims(d) != MLA_OK || B <= 0 || num_splits < 0) return 0;
-  if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads)) return 0;
+  if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads, d->cache_dtype == MLA_CACHE_FP8_E4M3)) return 0;
   const int parts = effective_parts(num_splits, B, d->n_heads);
   return mla::decode_workspace_layout(B, d->n_heads, d->d_c, parts).total;
 }
@@ -171,8 +171,7 @@ mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* po
       !aligned(workspace, 256) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)) ||
       (fp8 && !aligned(scales, 16)))
     return MLA_ERR_INVALID_ARG;
-  if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads)) return MLA_ERR_UNSUPPORTED;
-  if (fp8) return MLA_ERR_UNSUPPORTED;
+  if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads, fp8)) return MLA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_UNSUPPORTED;
   const int parts = effective_parts(num_splits, B, d->n_heads);
   const mla::WorkspaceLayout L = mla::decode_workspace_layout(B, d->n_heads, d->d_c, parts);

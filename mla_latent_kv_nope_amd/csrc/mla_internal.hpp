@@ -81,7 +81,7 @@ hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t s);
 // immediately before and after the split kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
-bool decode_supported(int d_c, int d_rope, int H);
+bool decode_supported(int d_c, int d_rope, int H, bool fp8);
 bool absorb_supported(int d_c, int d_nope);
 bool out_proj_supported(int d_c, int d_v);
 

@@ -123,6 +123,15 @@ def test_decode_validation():
         return f(ctypes.byref(d), a["q"], a["pool"], a["scales"], a["bt"], a["maxp"], a["nump"],
                  a["sl"], a["B"], a["ns"], a["ws"], a["wsb"], a["o"], a["lse"], None)
 
+    # fp8 caches decode only with the 576-element rows (d_c 512 + d_rope 64)
+    d8 = mla.make_dims(128, 512, 64, 128, 128, 64, fp8=True)
+    assert lib.mla_decode_workspace_size(ctypes.byref(d8), 4, 8) == need
+    t8 = mla.make_dims(4, 32, 16, 16, 16, 16, fp8=True)
+    assert lib.mla_decode_workspace_size(ctypes.byref(t8), 4, 8) == 0
+    _expect(f(ctypes.byref(t8), P, P, P, P, 8, 40, P, 4, 8, P, need, P, P, None),
+            _native.MLA_ERR_UNSUPPORTED)
+    _expect(f(ctypes.byref(d8), P, P, None, P, 8, 40, P, 4, 8, P, need, P, P, None),
+            _native.MLA_ERR_INVALID_ARG)                          # fp8 without scales
     _expect(call(wsb=need - 1), _native.MLA_ERR_WORKSPACE)
     _expect(call(ws=P + 16), _native.MLA_ERR_INVALID_ARG)         # workspace not 256-aligned
     _expect(call(q=None), _native.MLA_ERR_INVALID_ARG)

@@ -30,6 +30,19 @@ SMALL = [
 ]
 
 
+# fp8 cache (one fp32 scale per token): the split kernel stages fp8 tiles and
+# converts them to bf16 (code * scale, rounded) before the same MFMA path
+FP8_SMALL = [
+    configs.V3.with_(name="v3_fp8_small", fp8=True, batch=5, seq_len=None, seq_lens=(1, 31, 33, 1500, 64)),
+    configs.V3.with_(name="v3_fp8_p16", fp8=True, batch=4, seq_len=None, seq_lens=(17, 100, 5, 700),
+                     page_size=16),
+    configs.V3.with_(name="v3_fp8_h40", fp8=True, batch=3, n_heads=40, seq_len=None, seq_lens=(64, 77, 1)),
+    configs.V2LITE.with_(name="v2lite_fp8", fp8=True, batch=3, seq_len=None, seq_lens=(300, 1, 2000)),
+    configs.V2LITE.with_(name="v2lite_fp8_h32", fp8=True, batch=2, n_heads=32, seq_len=None,
+                         seq_lens=(129, 1000)),
+]
+
+
 def _compare(inp, res, batches=None, heads=None):
     ref = reference_decode(inp, batches=batches, heads=heads)
     bsel = slice(None) if batches is None else list(batches)
@@ -49,6 +62,31 @@ def test_end_to_end_matches_oracle(wl):
     d = dims_for(wl)
     print(f"[decode e2e] {wl.name}", flush=True)
     res = decode_step(inp, d)
+    _compare(inp, res)
+
+
+@pytest.mark.parametrize("wl", FP8_SMALL, ids=lambda w: w.name)
+def test_fp8_end_to_end_matches_oracle(wl):
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    print(f"[decode fp8 e2e] {wl.name}", flush=True)
+    res = decode_step(inp, d)
+    _compare(inp, res)
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 0])
+def test_fp8_split_invariance(num_splits):
+    wl = configs.V3.with_(name="v3_fp8_splits", fp8=True, batch=4, seq_len=None,
+                          seq_lens=(2000, 33, 1, 700))
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    print(f"[decode fp8 splits] num_splits={num_splits}", flush=True)
+    pool, scales, t = build_cache(inp, d)
+    base = decode_step(inp, d, num_splits=1, cache=(pool, scales, t))
+    res = decode_step(inp, d, num_splits=num_splits, cache=(pool, scales, t))
+    rel = np.linalg.norm(res["o_lat"] - base["o_lat"]) / np.linalg.norm(base["o_lat"])
+    assert rel <= 2e-3, rel
+    assert np.max(np.abs(res["lse"] - base["lse"])) <= 1e-5
     _compare(inp, res)
 
 
@@ -177,6 +215,17 @@ def test_ragged_full_size_sampled():
     res = decode_step(inp, d)
     assert np.all(np.isfinite(res["out"]))
     _compare(inp, res, batches=pick)
+
+
+@pytest.mark.slow
+def test_fp8long_full_size_sampled():
+    wl = configs.FP8LONG
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    print("[decode fp8long full] B=4 H=128 S=131072 fp8", flush=True)
+    res = decode_step(inp, d)
+    assert np.all(np.isfinite(res["out"]))
+    _compare(inp, res, batches=[2], heads=[0, 77, 127])
 
 
 @pytest.mark.parametrize("t_star", [0, 15, 16, 17, 30, 31, 36])
