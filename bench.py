@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=24,
                     help="sequences of the workload the oracle decodes for cpu_baseline (0 = skip)")
+    ap.add_argument("--flushed-iters", type=int, default=50,
+                    help="decode-only iterations, each after reading 768 MiB of other data "
+                         "(evicts the Infinity Cache), for the median / p10 / p90 (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three device-to-device copies of MIB MiB (a kernel of known "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -99,7 +102,53 @@ def cpu_baseline(inp, n_seq: int):
     toks = int(np.sum(inp.seq_lens[:n_seq]))
     return {"value": n_seq / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_seq} of {len(inp.seq_lens)} sequences x {inp.wl.n_heads} heads "
-                      f"({toks} cached tokens), explicit fp64 form, {dt:.2f} s"}
+                      f"({toks} cached tokens), explicit fp64 form, {dt:.2f} s",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+            "blas": _blas_name()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_name() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{p.get('internal_api')} ({p.get('num_threads')} threads)" for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:  # pragma: no cover
+        return "unknown"
+
+
+def flushed_decode_times(mla, torch, decode, iters: int):
+    """Per-call time of mla_decode_paged alone (HIP events on the current
+    stream), each call right after a full read of a 768 MiB scratch buffer, so
+    that no line of the previous call survives in the 256 MB Infinity Cache.
+    (A read keeps the GPU busy up to the call: after idle gaps or large
+    writes the clock state alone moved this time by up to 30 %.)"""
+    scratch = torch.ones(768 << 18, dtype=torch.int32, device="cuda:0")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for _ in range(3):
+        decode()
+    for e0, e1 in ev:
+        scratch.max()
+        e0.record()
+        decode()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    pick = lambda f: ms[min(len(ms) - 1, int(f * len(ms)))]
+    return {"median_ms": round(pick(0.5), 5), "p10_ms": round(pick(0.1), 5),
+            "p90_ms": round(pick(0.9), 5), "iters": iters,
+            "note": "plan + split + combine, each call after reading 768 MiB of other data"}
 
 
 def main():
@@ -172,6 +221,12 @@ def main():
     elapsed = time.perf_counter() - t0
     split_ms_total, n_rec = mla.profile_end()
     assert torch.isfinite(out.float()).all(), "non-finite output"
+    flushed = None
+    if args.flushed_iters > 0:
+        flushed = flushed_decode_times(
+            mla, torch, lambda: mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"],
+                                                 args.num_splits, ws, o_lat, lse),
+            args.flushed_iters)
 
     ms_step = 1e3 * elapsed / args.steps
     value = B * args.steps / elapsed
@@ -207,6 +262,16 @@ def main():
         "decode_kernel_tokens_per_s": round(B / (split_ms * 1e-3), 1),
         "roofline": roof,
     }
+    if flushed is not None:
+        # the whole mla_decode_paged call against the path's algorithmic bytes:
+        # cache + q in + o_lat out
+        t_med = flushed["median_ms"] * 1e-3
+        path_bytes = split_bytes + B * H * wl.d_c * 2
+        flushed.update({"tokens_per_s": round(B / t_med, 1),
+                        "achieved_GBs": round(path_bytes / t_med / 1e9, 1),
+                        "achieved_tflops": round(flops / t_med / 1e12, 1),
+                        "algorithmic_bytes": path_bytes})
+        rec["decode_paged_flushed"] = flushed
     if args.cpu_sample > 0:
         rec["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample, B))
     print(json.dumps(rec), flush=True)

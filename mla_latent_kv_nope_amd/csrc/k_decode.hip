@@ -8,10 +8,10 @@
 // split into partial results merged by their log-sum-exp is this library's
 // own design; the pages do not describe one.
 //
-// Three kernels, all enqueued on the caller's stream:
-//   k_plan    one workgroup: tiles per sequence (32 tokens each), their prefix
-//             sums, and the per-workgroup quota = ceil(total tiles / parts).
-//   k_split   workgroup w takes global tiles [w*quota, (w+1)*quota) of the
+// Two kernels, both enqueued on the caller's stream:
+//   k_split   every workgroup first derives the plan (tiles per sequence,
+//             32 tokens each; quota = ceil(total tiles / parts)); workgroup w
+//             then takes global tiles [w*quota, (w+1)*quota) of the
 //             concatenated batch; a range may cover the tail of one sequence
 //             and the head of the next.  A piece that is a whole sequence
 //             writes o_lat/lse directly; otherwise the piece's normalised O
@@ -160,40 +160,10 @@ __device__ __forceinline__ void sched_interleave() {
 __device__ __forceinline__ int clamp_len(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* seq_lens, int B, int cap,
-                                               int num_parts, int32_t* plan) {
-  __shared__ int32_t scan[1024];
-  __shared__ int32_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += 1024) {
-    const int b = base + threadIdx.x;
-    const int n = b < B ? (clamp_len(seq_lens[b], cap) + kTile - 1) / kTile : 0;
-    scan[threadIdx.x] = n;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      scan[threadIdx.x] += v;
-      __syncthreads();
-    }
-    if (b < B) plan[b] = carry + scan[threadIdx.x] - n;  // exclusive prefix
-    __syncthreads();
-    if (threadIdx.x == 1023) carry += scan[1023];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const int total = carry;
-    plan[B] = total;
-    plan[B + 1] = total > 0 ? (total + num_parts - 1) / num_parts : 1;
-  }
-}
-
-// ---------------------------------------------------------------------------
 template <int DC, int DR, int NW, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu((NW + 3) / 4, (NW + 3) / 4)))
-void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __restrict__ seq_lens,
+void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict__ seq_lens,
              const int32_t* __restrict__ block_table) {
   using Cfg = DecodeCfg<DC, DR, NW, FP8>;
   constexpr int R = Cfg::R, ROWB = Cfg::ROWB, CPR = Cfg::CPR;
@@ -220,14 +190,70 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
   const int HB = (H + 15) >> 4;               // 16-head blocks
   const int cap = a.max_pages << a.page_size_log2;
 
-  const int total = plan[B];
-  const int quota = plan[B + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // ---- plan, computed by every workgroup: tiles per sequence, the total,
+  // quota = ceil(total / parts) and the first (sequence, tile offset) of this
+  // workgroup's range [w * quota, (w + 1) * quota).  Thread i sums a chunk of
+  // C consecutive sequences; a wave scan plus the wave totals (in the P slots,
+  // unused until the first tile) give each chunk's first tile.  Workgroup 0
+  // also stores the prefix sums and the quota for k_combine.
+  auto tiles_of = [&](int bb) { return (clamp_len(seq_lens[bb], cap) + kTile - 1) / kTile; };
+  int* const scan = reinterpret_cast<int*>(pbuf);
+  const int C = (B + Cfg::THREADS - 1) / Cfg::THREADS;
+  const int k0 = static_cast<int>(threadIdx.x) * C;
+  int csum = 0;
+  for (int j = 0; j < C; ++j)
+    if (k0 + j < B) csum += tiles_of(k0 + j);
+  int incl = csum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) scan[wave] = incl;
+  __syncthreads();
+  int total = 0, before = 0;
+  for (int i = 0; i < NW; ++i) {
+    const int v = scan[i];
+    total += v;
+    if (i < wave) before += v;
+  }
+  const int excl = before + incl - csum;       // tiles before this thread's chunk
+  const int quota = total > 0 ? (total + a.num_parts - 1) / a.num_parts : 1;
+  if (w == 0) {
+    int p0 = excl;
+    for (int j = 0; j < C; ++j)
+      if (k0 + j < B) {
+        plan[k0 + j] = p0;
+        p0 += tiles_of(k0 + j);
+      }
+    if (threadIdx.x == 0) {
+      plan[B] = total;
+      plan[B + 1] = quota;
+    }
+  }
   int g = w * quota;
   const int gend = min(g + quota, total);
   if (g >= gend) return;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __syncthreads();                              // wave totals read before reuse
+  // the chunk holding tile g names the sequence containing it
+  if (excl <= g && g < excl + csum) {
+    int p0 = excl;
+    for (int j = 0; j < C; ++j) {
+      const int n = k0 + j < B ? tiles_of(k0 + j) : 0;
+      if (g < p0 + n) {
+        scan[0] = k0 + j;
+        scan[1] = p0;
+        break;
+      }
+      p0 += n;
+    }
+  }
+  __syncthreads();
+  int b = scan[0];
+  int t0 = scan[1];                             // first tile of sequence b
   const int quad = lane >> 4;          // k slice (operands) / token quad (S) / head quad (O)
   const int l16 = lane & 15;
   const int lg = a.page_size_log2;
@@ -245,16 +271,6 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
     reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  // first sequence of this range: the largest b with plan[b] <= g
-  int b;
-  {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (plan[mid] <= g) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-  }
 
   // Per-lane LDS byte offsets (relative to a tile buffer) of the MFMA operand
   // reads; every other operand address is one of these plus an immediate.  They
@@ -304,7 +320,7 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
   };
 
   while (g < gend) {
-    const int t0 = plan[b], t1 = plan[b + 1];
+    const int t1 = t0 + tiles_of(b);
     const int lt0 = g - t0, lt1 = min(gend, t1) - t0;
     const int ntiles = lt1 - lt0;
     const int S = clamp_len(seq_lens[b], cap);
@@ -780,8 +796,9 @@ void k_split(DecodeArgs a, const int32_t* __restrict__ plan, const int32_t* __re
 
     // next piece: the next non-empty sequence
     g = t0 + lt1;
+    t0 = t1;
     ++b;
-    while (b < B && plan[b + 1] <= g) ++b;
+    while (b < B && tiles_of(b) == 0) ++b;
     // all waves must be done reading the ring and the shared 1/l before the
     // next piece refills them
     __syncthreads();
@@ -908,7 +925,7 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
 template <int DC, int DR, int NW, bool FP8 = false>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_split<DC, DR, NW, FP8>), dim3(a.num_parts), dim3(64 * NW), 0, s, a,
-                     static_cast<const int32_t*>(a.plan), a.seq_lens, a.block_table);
+                     a.plan, a.seq_lens, a.block_table);
   return hipGetLastError();
 }
 
@@ -950,10 +967,7 @@ WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, a.seq_lens, a.B, a.max_pages << a.page_size_log2,
-                     a.num_parts, a.plan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (a.d_c == 512 && a.d_rope == 64 && a.fp8) {
     if (a.H <= 16) e = launch_split<512, 64, 1, true>(a, s);
