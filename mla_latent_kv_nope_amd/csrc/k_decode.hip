@@ -806,83 +806,59 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split sequences.  One wave per (sequence, 16-head group, 8 column
-// blocks): the pieces' lse give each head's merged lse and the piece weights
-// exp(lse_p - lse); the pieces' O are read in the split kernel's accumulator
-// order (bf16, 8-byte loads, 512 bytes per wave instruction) and summed in
-// piece order in fp32.
-// Sequences with no tokens get o_lat = 0 and lse = -inf; whole-sequence pieces
-// were written by k_split.
+// Merge of split sequences.  One workgroup per (sequence, 16-head block); wave
+// q handles column blocks [8q, 8q + 8).  The pieces' lse give each head's
+// merged lse and the piece weights exp(lse_p - lse); the pieces' O are read in
+// the split kernel's accumulator order (bf16, 8-byte loads, 512 bytes per wave
+// instruction), all pieces of a group in flight together, and summed in piece
+// order in fp32.  The merged block goes through LDS so that o_lat is written
+// with 16-byte stores.  Sequences with no tokens get o_lat = 0 and lse = -inf;
+// whole-sequence pieces were written by k_split.
 template <int DC>
-__global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
+__global__ __launch_bounds__(64 * (DC / 128 > 0 ? DC / 128 : 1)) void k_combine(DecodeArgs a) {
   constexpr int VCB = DC / 16;
   constexpr int CPW = VCB < 8 ? VCB : 8;   // column blocks per wave
-  constexpr int NQ = VCB / CPW;
+  constexpr int NWV = VCB / CPW;           // waves
+  constexpr int THREADS = 64 * NWV;
   constexpr uint32_t kPieceBytes = VCB * 64 * 8;
+  constexpr int ROW = DC + 16;             // LDS row stride (elements): quads land on distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t tile[16 * ROW];
   const int H = a.H, HG16 = (H + 15) >> 4;
-  int id = blockIdx.x;
-  const int cq = id % NQ;
-  id /= NQ;
-  const int gw = id % HG16;
-  const int b = id / HG16;
-  const int lane = threadIdx.x, quad = lane >> 4, l16 = lane & 15;
+  const int gw = blockIdx.x % HG16;
+  const int b = blockIdx.x / HG16;
+  const int lane = threadIdx.x & 63, cq = threadIdx.x >> 6, quad = lane >> 4, l16 = lane & 15;
   const int hq = gw * 16 + 4 * quad;       // first of this lane's 4 heads
   const int t0 = a.plan[b], t1 = a.plan[b + 1], quota = a.plan[a.B + 1];
+  const int hn = min(16, H - gw * 16);     // heads of this block
 
-  // o_lat of this lane's heads: channel 16cb + l16 of heads hq + i; heads
-  // past H get an offset beyond the buffer's range (the store is dropped)
-  const auto ro = make_rsrc(a.o_lat + (static_cast<int64_t>(b) * H + gw * 16) * DC, 16 * DC * 2);
-  auto store = [&](const f32x4* v) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t vo = hq + i < H ? static_cast<uint32_t>((4 * quad + i) * DC + l16) * 2 : 0x80000000u;
-#pragma unroll
-      for (int c = 0; c < CPW; ++c)
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(v[c][i])), ro, vo,
-                                              32 * (cq * CPW + c), 0);
+  // block -> o_lat rows of heads gw*16 .. +hn, 16 bytes per store
+  auto flush = [&]() {
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(a.o_lat + (static_cast<int64_t>(b) * H + gw * 16) * DC);
+    for (int i = threadIdx.x; i < hn * DC / 8; i += THREADS) {
+      const int h = i / (DC / 8), c8 = i - h * (DC / 8);
+      dst[i] = *reinterpret_cast<const uint4*>(&tile[h * ROW + 8 * c8]);
     }
   };
 
   if (t1 == t0) {
-    f32x4 z[CPW] = {};
-    store(z);
-    if (a.lse != nullptr && cq == 0 && l16 == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (hq + i < H) a.lse[static_cast<int64_t>(b) * H + hq + i] = -INFINITY;
-    }
+    for (int i = threadIdx.x; i < 16 * ROW / 8; i += THREADS)
+      reinterpret_cast<uint4*>(tile)[i] = make_uint4(0, 0, 0, 0);
+    flush();
+    if (a.lse != nullptr && threadIdx.x < hn) a.lse[static_cast<int64_t>(b) * H + gw * 16 + threadIdx.x] = -INFINITY;
     return;
   }
   const int wf = t0 / quota, wl = (t1 - 1) / quota;
   if (wf == wl || gw * 16 >= H) return;
 
-  // pieces in groups of PG: every load of a group is issued before any use,
-  // so each group costs one memory round trip
-  constexpr int PG = 4;
+  constexpr int PG = 4;                    // pieces per round trip
   const int np = wl - wf + 1;
   const int64_t lse0 = (static_cast<int64_t>(wf) + b) * H;
   int hc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) hc[i] = min(hq + i, H - 1);
-  f32x4 mx = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int k0 = 0; k0 < np; k0 += PG) {
-    f32x4 l[PG];
-#pragma unroll
-    for (int k = 0; k < PG; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        l[k][i] = k0 + k < np ? a.part_lse[lse0 + (k0 + k) * H + hc[i]] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < PG; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], l[k][i]);
-  }
-  f32x4 acc[CPW];
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
   const uint32_t voff = static_cast<uint32_t>(lane) * 8;
-  for (int k0 = 0; k0 < np; k0 += PG) {
-    f32x4 t[PG][CPW];
-    f32x4 l[PG];
+  auto load_group = [&](int k0, f32x4 (&t)[PG][CPW], f32x4 (&l)[PG]) {
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
       const bool ok = k0 + k < np;
@@ -891,9 +867,29 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < CPW; ++c) t[k][c] = buffer_load_bf16x4(rs, voff, (cq * CPW + c) * 512);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        l[k][i] = ok ? a.part_lse[lse0 + (k0 + k) * H + hc[i]] : -INFINITY;
+      for (int i = 0; i < 4; ++i) l[k][i] = ok ? a.part_lse[lse0 + (k0 + k) * H + hc[i]] : -INFINITY;
     }
+  };
+  f32x4 mx = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  f32x4 t[PG][CPW], l[PG];
+  load_group(0, t, l);
+  if (np > PG) {          // rare: the maximum over every piece first
+    for (int k0 = PG; k0 < np; k0 += PG) {
+#pragma unroll
+      for (int k = 0; k < PG; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + k < np) mx[i] = fmaxf(mx[i], a.part_lse[lse0 + (k0 + k) * H + hc[i]]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PG; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], l[k][i]);
+  f32x4 acc[CPW];
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < np; k0 += PG) {
+    if (k0 > 0) load_group(k0, t, l);
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
       if (k0 + k >= np) break;
@@ -913,8 +909,11 @@ __global__ __launch_bounds__(64) void k_combine(DecodeArgs a) {
     lse_all[i] = mx[i] + logf(sum[i]);
   }
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) acc[c] *= inv;
-  store(acc);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      tile[(4 * quad + i) * ROW + 16 * (cq * CPW + c) + l16] = f32_to_bf16_bits(acc[c][i] * inv[i]);
+  flush();
   if (a.lse != nullptr && cq == 0 && l16 == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -989,7 +988,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hip
   if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
   const int hg16 = (a.H + 15) / 16;
   if (a.d_c == 512)
-    hipLaunchKernelGGL(k_combine<512>, dim3(a.B * hg16 * 4), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_combine<512>, dim3(a.B * hg16), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_combine<32>, dim3(a.B * hg16), dim3(64), 0, s, a);
   return hipGetLastError();
