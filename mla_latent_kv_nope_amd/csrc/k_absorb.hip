@@ -45,7 +45,6 @@ template <int DC, int DN>
 __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a, int n_gemm) {
   constexpr int COLS = DC < 128 ? DC : 128;  // latent columns per workgroup
   constexpr int NCB = DC / COLS;             // column blocks per head
-  constexpr int KC = DN / 16;                // reduction chunks
   static_assert(COLS % 32 == 0 && DN % 16 == 0, "tile shape");
   const int B = a.B, H = a.H;
   const int R = DC + a.d_rope;
@@ -92,34 +91,70 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a, int n_gemm) {
     return;
   }
 
+  // GEMM workgroup: head h, latent columns [cbk*COLS, +COLS), batch rows
+  // [b0, b0 + 32).  The W_UK slice and the q_nope rows are copied into LDS with
+  // 16-byte global->LDS copies (row r's 16-byte chunk j stored at chunk
+  // j ^ (r % CH)), read back as MFMA operands without bank conflicts, and the
+  // 32 x COLS result goes back through LDS to leave as 16-byte stores.
+  constexpr int CH = DN / 8;                 // 16-byte chunks per row
+  constexpr int ROWB = DN * 2;
+  static_assert((CH & (CH - 1)) == 0 && (COLS * ROWB) % 1024 == 0 && (32 * ROWB) % 1024 == 0,
+                "copy shapes");
+  __shared__ __attribute__((aligned(1024))) char wl[COLS * ROWB];   // W_UK slice [COLS][DN]
+  __shared__ __attribute__((aligned(1024))) char ql[32 * ROWB];     // q_nope rows [32][DN]
+  __shared__ __attribute__((aligned(16))) uint16_t ol[32 * (COLS + 8)];  // result [32][COLS]
   int id = blockIdx.x;
   const int cbk = id % NCB;
   id /= NCB;
   const int h = id % H;
   const int b0 = (id / H) * 32;              // batch rows [b0, b0 + 32)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave >= COLS / 32) return;
-  const int c = cbk * COLS + wave * 32 + (lane & 31);
-  const int half = lane >> 5;
-  const int br = b0 + (lane & 31);
-  const bool ok = br < B;
-  bf16x8 wreg[KC], qv[KC];
-  const uint16_t* wrow = a.w_uk + (static_cast<int64_t>(h) * DC + c) * DN + 8 * half;
-  const uint16_t* qrow = a.q_nope + (static_cast<int64_t>(ok ? br : 0) * H + h) * DN + 8 * half;
-  const bf16x8 z = {};
-#pragma unroll
-  for (int k = 0; k < KC; ++k) {
-    wreg[k] = *reinterpret_cast<const bf16x8*>(wrow + 16 * k);
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * k);
-    qv[k] = ok ? v : z;   // rows past the batch contribute zeros
+  constexpr int NWAVES = 4;
+
+  // copies: lane l of 1 KB block k fills row (1024k + 16l) / ROWB, chunk
+  // position p = l % CH with source chunk p ^ (row % CH)
+  const uint16_t* wsrc = a.w_uk + (static_cast<int64_t>(h) * DC + cbk * COLS) * DN;
+  for (int k = wave; k < COLS * ROWB / 1024; k += NWAVES) {
+    const int r = (1024 * k + 16 * lane) / ROWB, pch = lane % CH;
+    const uint16_t* src = wsrc + r * DN + 8 * (pch ^ (r % CH));
+    lds_dma16_v(src, lds_addr(wl + 1024 * k));
   }
-  f32x16 acc = {};
+  for (int k = wave; k < 32 * ROWB / 1024; k += NWAVES) {
+    const int r = (1024 * k + 16 * lane) / ROWB, pch = lane % CH;
+    const int br = b0 + r < B ? b0 + r : b0;   // rows past the batch: any valid row
+    const uint16_t* src = a.q_nope + (static_cast<int64_t>(br) * H + h) * DN + 8 * (pch ^ (r % CH));
+    lds_dma16_v(src, lds_addr(ql + 1024 * k));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  if (wave < COLS / 32) {
+    // A = q rows (lane: row l%32, k = 8(l/32) + [0,8) of each 16-wide step),
+    // B = W_UK rows (lane: column l%32, same k)
+    const int r = lane & 31, half = lane >> 5;
+    const int cw = wave * 32 + r;
+    f32x16 acc = {};
 #pragma unroll
-  for (int k = 0; k < KC; ++k) acc = mfma32(qv[k], wreg[k], acc);
+    for (int k = 0; k < DN / 16; ++k) {
+      const int ch = 2 * k + half;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(ql + r * ROWB + 16 * (ch ^ (r % CH)));
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(wl + cw * ROWB + 16 * (ch ^ (cw % CH)));
+      acc = mfma32(av, bv, acc);
+    }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int b = b0 + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (b < B) a.q_out[(static_cast<int64_t>(b) * H + h) * R + c] = f32_to_bf16_bits(acc[i]);
+    for (int i = 0; i < 16; ++i) {
+      const int rr = 8 * (i >> 2) + 4 * half + (i & 3);
+      ol[rr * (COLS + 8) + cw] = f32_to_bf16_bits(acc[i]);
+    }
+  }
+  __syncthreads();
+  // rows of the result: COLS columns = COLS * 2 bytes each, 16 bytes per store
+  constexpr int SPR = COLS / 8;              // 16-byte stores per row
+  for (int i = threadIdx.x; i < 32 * SPR; i += 64 * NWAVES) {
+    const int rr = i / SPR, c8 = i - rr * SPR;
+    if (b0 + rr < B)
+      *reinterpret_cast<uint4*>(a.q_out + (static_cast<int64_t>(b0 + rr) * H + h) * R + cbk * COLS + 8 * c8) =
+          *reinterpret_cast<const uint4*>(&ol[rr * (COLS + 8) + 8 * c8]);
   }
 }
 
