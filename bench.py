@@ -3,7 +3,7 @@
 
 A step is the whole hot path for one new token per sequence:
   mla_append_latent (the B new rows) -> mla_absorb_q -> mla_decode_paged
-  (plan + split attention + LSE combine) -> mla_out_proj,
+  (split attention with its own tile plan + LSE combine) -> mla_out_proj,
 on the DeepSeek-V3-shaped workload (B=64, H=128, d_c=512, d_rope=64,
 d_nope=d_v=128, S=8192, page 64, bf16 latent cache, permuted pages), with all
 inputs resident in HBM.  The cache holds S-1 tokens per sequence before the
@@ -148,7 +148,7 @@ def flushed_decode_times(mla, torch, decode, iters: int):
     pick = lambda f: ms[min(len(ms) - 1, int(f * len(ms)))]
     return {"median_ms": round(pick(0.5), 5), "p10_ms": round(pick(0.1), 5),
             "p90_ms": round(pick(0.9), 5), "iters": iters,
-            "note": "plan + split + combine, each call after reading 768 MiB of other data"}
+            "note": "split + combine, each call after reading 768 MiB of other data"}
 
 
 def main():
