@@ -60,6 +60,21 @@ constexpr float kHeadroom = 64.0f;  // log2 units
 #endif
 constexpr int kQkAhead = MLA_QK_AHEAD;
 constexpr int kPvAhead = MLA_PV_AHEAD;
+// specialised path: K operand reads in flight ahead of the 32x32x16 MFMAs, and
+// whether the loader waves issue a tile's copies after their PV instead of
+// right after the barrier
+#ifndef MLA_QK32_AHEAD
+#define MLA_QK32_AHEAD 2
+#endif
+#ifndef MLA_SPEC_LATE_ISSUE
+#define MLA_SPEC_LATE_ISSUE 0
+#endif
+constexpr int kQk32Ahead = MLA_QK32_AHEAD;
+constexpr bool kSpecLateIssue = MLA_SPEC_LATE_ISSUE != 0;
+#ifndef MLA_SPEC_QK_PRIO
+#define MLA_SPEC_QK_PRIO 0
+#endif
+constexpr int kSpecQkPrio = MLA_SPEC_QK_PRIO;   // issue priority of the QK waves
 
 template <int DC, int DR, int NW, bool FP8 = false>
 struct DecodeCfg {
@@ -76,7 +91,12 @@ struct DecodeCfg {
   static constexpr int THREADS = 64 * NW;
   // tile loads are issued by the last LW waves (the others start computing
   // right after each barrier); loader i issues blocks i, i + LW, ...
-  static constexpr int LW = (MLA_LOADER_WAVES > 0 && MLA_LOADER_WAVES < NW) ? MLA_LOADER_WAVES : NW;
+  // Specialised V3-shaped layout (d_c 512, d_rope 64, 8 waves, bf16 cache):
+  // waves 0-3 score 32 heads each on 32x32x16 MFMAs, waves 4-7 only
+  // accumulate O and issue the tile loads.
+  static constexpr bool SPEC = NW == 8 && DC == 512 && DR == 64 && !FP8;
+  static constexpr int LW = SPEC ? 4
+                            : (MLA_LOADER_WAVES > 0 && MLA_LOADER_WAVES < NW) ? MLA_LOADER_WAVES : NW;
   static constexpr int LD_HI = (INSTR + LW - 1) / LW;  // loads of loaders < INSTR % LW (or all)
   static constexpr int LD_LO = INSTR / LW;
   static constexpr int K32 = R / 32;                 // full 32-wide QK chunks
@@ -181,7 +201,15 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   int* const vote = reinterpret_cast<int*>(pbuf);
   float* const inv_share = reinterpret_cast<float*>(pbuf + PSLOT);
 
-  const int w = blockIdx.x;
+  // Piece index of this workgroup.  Workgroups are dispatched round-robin
+  // over the 8 XCDs (blockIdx % 8); consecutive pieces, which are mostly the
+  // pieces of one sequence, go to the same XCD so that they share its L2 for
+  // the query and the block-table row.  A bijection on [0, num_parts).
+  const int w = [&] {
+    const int i = blockIdx.x, P = a.num_parts;
+    const int x = i & 7, q8 = P >> 3, r8 = P & 7;
+    return x * q8 + min(x, r8) + (i >> 3);
+  }();
 
   // plan, seq_lens and block_table are read with scalar loads (restrict lets
   // the compiler prove nothing here writes them); scalar loads wait on their
@@ -346,6 +374,23 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
                                            : nullptr;
     };
     auto issue_general = [&](int tok0, char* dst_tile) {
+      if constexpr (Cfg::SPEC) {
+        // loader i copies the tile's 8-row group i (see the fast path)
+        if (loader >= 0) {
+          const LdLane ll = ld_lane();
+          const char* row0 = page_base(tok0);
+          const char* fb = row0 ? row0 : pool;
+          const int rtok = tok0 + 8 * loader;      // first token of the row group
+          const char* rb = rtok >= S ? nullptr
+                           : (ps >= kTile || loader < 2) ? row0 + 8 * loader * ROWB : page_base(rtok);
+          const bool ok = rb != nullptr && row0 != nullptr && rtok + ll.r < S;
+          const char* src = ok ? rb + ll.off : fb + ll.fb;
+          const uint32_t dst = lds_addr(dst_tile) + static_cast<uint32_t>(loader) * Cfg::CG * 1024;
+#pragma unroll
+          for (int k = 0; k < Cfg::CG; ++k) lds_dma16_v(src + k * 128, dst + k * 1024);
+        }
+        return;
+      }
       const LdLane ll = ld_lane();
       const int ld_r = ll.r;
       const uint32_t ld_off = ll.off, ld_fb = ll.fb;
@@ -389,6 +434,19 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
           if (pg >= 0 && pg < a.num_pages) {
             const char* tile0 = pool + pg * page_bytes + (tok0 & (ps - 1)) * ROWB;
             const uint32_t ld_off = ld_lane().off;
+            if constexpr (Cfg::SPEC) {
+              // loader i copies the 8-row group i (9 KB contiguous in the
+              // page): blocks 9i .. 9i + 8, source and LDS offsets with
+              // constant strides
+              static_assert(Cfg::LD_HI == Cfg::CG && Cfg::INSTR == Cfg::LW * Cfg::CG, "one row group per loader");
+              if (loader >= 0) {
+                const char* src = tile0 + loader * 8 * ROWB;
+                const uint32_t dst = lds_addr(dst_tile) + static_cast<uint32_t>(loader) * Cfg::CG * 1024;
+#pragma unroll
+                for (int k = 0; k < Cfg::CG; ++k) lds_dma16(src + k * 128, ld_off, dst + k * 1024);
+              }
+              return;
+            }
 #pragma unroll
             for (int k = 0; k < Cfg::LD_HI; ++k) {
               const int blk = k * Cfg::LW + loader;
@@ -464,6 +522,261 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       }
     };
 
+    if constexpr (Cfg::SPEC) {
+    // ---- Specialised roles.  QK waves (0-3): S^T (32 tokens x 32 heads) on
+    // 32x32x16 MFMAs with the K tile as the A operand from LDS and Q (32 heads
+    // x 576) in 144 VGPRs, softmax, P published to LDS, and O for column
+    // blocks [2w, 2w + 2).  PV waves (4-7): O for column blocks
+    // [8 + 6(w - 4), +6), and every tile load.  One barrier per tile as in the
+    // general path: step it computes S(it) and PV(it - 1).
+    constexpr int QH = 32, NQW = 4, QCB = 2, PCB = 6;
+    constexpr int KS = R / 16;                    // 16-wide k-steps
+    constexpr int AHEAD = Cfg::NBUF - 2;
+    static_assert(NQW * QH == 16 * NW && NQW * QCB + (NW - NQW) * PCB == Cfg::VCB && Cfg::BLOCKED &&
+                  Cfg::LW == NW - NQW && Cfg::INSTR % Cfg::LW == 0 && AHEAD >= 1, "specialised shape");
+    const bool qkw = wave < NQW;
+
+    auto sync_tile = [&](int it) {
+      if (!qkw) wait_tiles<AHEAD + 2, Cfg::LD_HI>(min(ntiles - 1 - it, AHEAD - 1));
+      block_barrier();
+    };
+    // a score far above the offset anywhere in the workgroup: redo the piece
+    // with each head's true maximum as its offset (cannot overflow again)
+    auto vote_again = [&](bool overflow) -> bool {
+      __syncthreads();                 // P slots are free from here on
+      if (threadIdx.x == 0) *vote = 0;
+      __syncthreads();
+      if (__builtin_amdgcn_ballot_w64(overflow) != 0 && lane == 0) *vote = 1;
+      __syncthreads();
+      const bool again = *vote != 0;
+      __syncthreads();
+      return again;
+    };
+    // O += P . V over all head blocks and column blocks [cbf, cbf + NC): B (V,
+    // transpose reads) held for the wave's column blocks while the head
+    // blocks' A operands (P rows) stream past, read AD head blocks ahead.
+    auto pv_cols = [&](const char* tb, int pslot, int cbf, auto& oo) {
+      constexpr int NC = sizeof(oo[0]) / sizeof(oo[0][0]);
+      const uint32_t pb = pv_base0();
+      bf16x8 vb[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int cb = cbf + c;
+        const char* p0 = tb + ((pb ^ static_cast<uint32_t>(32 * (cb & 3))) + 1024 * (cb >> 2));
+        const bf16x4 v0 = lds_read_tr16(p0);
+        const bf16x4 v1 = lds_read_tr16(p0 + 16 * ROWB);
+        vb[c] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const char* pa_base = pbuf + pslot * PSLOT + p_lane_off();
+      constexpr int AD = 3;
+      bf16x8 abuf[AD];
+#pragma unroll
+      for (int i = 0; i < AD; ++i) abuf[i] = *reinterpret_cast<const bf16x8*>(pa_base + i * 16 * PROW);
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb) {
+        const bf16x8 pa = abuf[hb % AD];
+        if (hb + AD < NW) abuf[hb % AD] = *reinterpret_cast<const bf16x8*>(pa_base + (hb + AD) * 16 * PROW);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) oo[hb][c] = mfma16(pa, vb[c], oo[hb][c]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // normalised O of this wave's column blocks to o_lat (whole sequence) or
+    // to the piece's partial slot, in accumulator order
+    auto store_o = [&](int cbf, auto& oo) {
+      constexpr int NC = sizeof(oo[0]) / sizeof(oo[0][0]);
+      const int fl = lane_id_fresh();
+      const int fq = fl >> 4, f16 = fl & 15;
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb) {
+        if (hb < HB) {
+          f32x4 scv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) scv[i] = inv_share[hb * 16 + 4 * fq + i];
+#pragma unroll
+          for (int c = 0; c < NC; ++c) oo[hb][c] *= scv;
+        }
+      }
+      if (whole) {
+        const auto rs = make_rsrc(a.o_lat + static_cast<int64_t>(b) * H * DC, H * DC * 2);
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb) {
+          if (hb < HB) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int h = hb * 16 + 4 * fq + i;
+              const uint32_t vo = h < H ? static_cast<uint32_t>(h * DC + 16 * cbf + f16) * 2 : 0x80000000u;
+#pragma unroll
+              for (int c = 0; c < NC; ++c)
+                __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(oo[hb][c][i])), rs,
+                                                      vo, 32 * c, 0);
+            }
+          }
+        }
+      } else {
+        constexpr uint32_t kBlk = 64 * 8;                      // one 16 x 16 block, bf16
+        const int64_t slot = static_cast<int64_t>(w) + b;
+        const auto rs = make_rsrc(a.part_o + slot * HB * Cfg::VCB * (kBlk / 2), HB * Cfg::VCB * kBlk);
+        const uint32_t voff = static_cast<uint32_t>(fl) * 8;
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb) {
+          if (hb < HB) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+              buffer_store_bf16x4(oo[hb][c], rs, voff, (hb * Cfg::VCB + cbf + c) * kBlk);
+          }
+        }
+      }
+    };
+
+    if (qkw) {
+      if constexpr (kSpecQkPrio > 0) __builtin_amdgcn_s_setprio(kSpecQkPrio);
+      const int hq = QH * wave;                   // first head of this wave
+      // Q of two 16-head groups g: lane holds head hq + 16g + l16, elements
+      // [32kc + 8quad, +8) of chunk kc
+      bf16x8 qg[2][Cfg::K32];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int h = hq + 16 * g + l16;
+        const bool hv = h < H;
+        const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * H + (hv ? h : 0)) * R + 8 * quad;
+        const bf16x8 z = {};
+#pragma unroll
+        for (int kc = 0; kc < Cfg::K32; ++kc) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * kc);
+          qg[g][kc] = hv ? v : z;
+        }
+      }
+      f32x4 oo[NW][QCB];
+      float m_use[2] = {-INFINITY, -INFINITY};   // exponent offset per head group (set by the first tile)
+      float m_seen[2] = {-INFINITY, -INFINITY};  // running maxima
+      float l_part[2] = {0.f, 0.f};              // this lane's shares of the denominators
+      bool overflow = false;
+      // S^T (32 tokens x 32 heads) of one tile as four 16x16 accumulator
+      // chains (token block x head group): each K operand read (row 16tbk +
+      // l16, 16-byte chunk 4kc + quad) feeds the MFMAs of both head groups.
+      // Then the softmax of each group and P to slot pslot.
+      auto score2 = [&](const char* tb, int tok0, bool set_offset, int pslot) {
+        const QkBases qb = qk_bases();
+        auto a_ptr = [&](int i) {
+          const int kc = i >> 1, tbk = i & 1;
+          return reinterpret_cast<const bf16x8*>(tb + ((kc & 1) ? qb.odd : qb.even) + tbk * 16 * ROWB +
+                                                 1024 * (kc >> 1));
+        };
+        constexpr int NQ = 2 * Cfg::K32;
+        constexpr int QD = kQk32Ahead;
+        f32x4 sacc[2][2] = {};
+        bf16x8 abuf[QD];
+#pragma unroll
+        for (int i = 0; i < QD; ++i) abuf[i] = *a_ptr(i);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const bf16x8 av = abuf[i % QD];
+          if (i + QD < NQ) abuf[i % QD] = *a_ptr(i + QD);
+          sacc[0][i & 1] = mfma16(av, qg[0][i >> 1], sacc[0][i & 1]);
+          sacc[1][i & 1] = mfma16(av, qg[1][i >> 1], sacc[1][i & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // sacc[g][tbk][i] is token 16tbk + 4quad + i of head hq + 16g + l16
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float x[8];
+          float mt = -INFINITY;
+#pragma unroll
+          for (int tbk = 0; tbk < 2; ++tbk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = 16 * tbk + 4 * quad + i;
+              const float v = (tok0 + kTile <= S || tok0 + t < S) ? sacc[g][tbk][i] : -INFINITY;
+              x[4 * tbk + i] = v;
+              mt = fmaxf(mt, v);
+            }
+          mt = max_across_half_waves(max_across_quarter_pairs(mt)) * a.scale_log2;
+          m_seen[g] = fmaxf(m_seen[g], mt);
+          if (set_offset) m_use[g] = mt;            // first tile: O is still zero
+          overflow |= mt > m_use[g] + kHeadroom;
+          uint32_t pu[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j], a.scale_log2, -m_use[g]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j + 1], a.scale_log2, -m_use[g]));
+            l_part[g] += p0 + p1;
+            pu[j] = pack_bf16x2(p0, p1);
+          }
+          // P in PV A-operand order: k slot 8quad + j <-> token (j < 4 ? 4quad + j : 16 + 4quad + j - 4)
+          *reinterpret_cast<bf16x8*>(pbuf + pslot * PSLOT + (hq + 16 * g) * PROW + p_lane_off()) =
+              __builtin_bit_cast(bf16x8, pu);
+        }
+      };
+
+      for (int pass = 0;; ++pass) {
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+          for (int c = 0; c < QCB; ++c) oo[hb][c] = f32x4{};
+        l_part[0] = l_part[1] = 0.f;
+        overflow = false;
+        sync_tile(0);
+        score2(lds, lt0 * kTile, pass == 0, 0);
+        for (int it = 1; it < ntiles; ++it) {
+          sync_tile(it);
+          score2(lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES, (lt0 + it) * kTile, false, it & 1);
+          pv_cols(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (it - 1) & 1, QCB * wave, oo);
+        }
+        block_barrier();
+        pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1, QCB * wave, oo);
+        const bool again = vote_again(overflow);
+        if (!again || pass > 0) break;   // the second pass starts at the true maximum
+        m_use[0] = m_seen[0];
+        m_use[1] = m_seen[1];
+      }
+      // 1/l and lse of this wave's heads (four lanes hold a head)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float l_tot = sum_across_half_waves(sum_across_quarter_pairs(l_part[g]));
+        const float lse_nat = (m_use[g] + log2f(l_tot)) * kLn2;
+        const int h = hq + 16 * g + l16;
+        if (quad == 0) {
+          inv_share[h] = 1.0f / l_tot;
+          if (h < H) {
+            if (whole) {
+              if (a.lse != nullptr) a.lse[static_cast<int64_t>(b) * H + h] = lse_nat;
+            } else {
+              a.part_lse[(static_cast<int64_t>(w) + b) * H + h] = lse_nat;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      store_o(QCB * wave, oo);
+    } else {
+      const int cbf = NQW * QCB + PCB * (wave - NQW);
+      f32x4 oo[NW][PCB];
+      for (int pass = 0;; ++pass) {
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+          for (int c = 0; c < PCB; ++c) oo[hb][c] = f32x4{};
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i)
+          if (i < ntiles) issue_tile(lt0 + i, i);
+        sync_tile(0);
+        if (AHEAD < ntiles) issue_tile(lt0 + AHEAD, AHEAD % Cfg::NBUF);
+        for (int it = 1; it < ntiles; ++it) {
+          sync_tile(it);
+          if (!kSpecLateIssue && it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
+          pv_cols(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (it - 1) & 1, cbf, oo);
+          if (kSpecLateIssue && it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
+        }
+        block_barrier();
+        pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1, cbf, oo);
+        const bool again = vote_again(false);
+        if (!again || pass > 0) break;
+      }
+      __syncthreads();
+      store_o(cbf, oo);
+    }
+    } else {
     // query registers (QK waves): lane holds head hbase + l16, elements
     // [32kc + 8*quad, +8)
     bf16x8 qreg[Cfg::K32];
@@ -793,6 +1106,8 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         }
       }
     }
+
+    }  // general path
 
     // next piece: the next non-empty sequence
     g = t0 + lt1;
