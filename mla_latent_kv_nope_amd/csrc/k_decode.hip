@@ -20,22 +20,28 @@
 //             in piece order, and writes o_lat = 0, lse = -inf for sequences
 //             with no tokens.
 //
-// k_split design (gfx950): a workgroup of NW waves x 16 heads works on one
-// (sequence piece, head group); with NW = 8 one workgroup holds all 128 heads, so
-// each 32-token tile of 576-element rows is fetched from HBM once and shared by
-// every head.  Tiles are gathered page by page with direct global->LDS 16-byte
-// loads into a ring of NBUF buffers (the next NBUF-1 tiles are in flight while
-// one is consumed); 16-byte chunks are XOR-swizzled within groups of 8 so that
-// the row-strided MFMA operand reads spread over the LDS banks.  Per tile and wave:
-//   S^T (2 x 16 tokens x 16 heads) = K_tile . Q^T   on 16x16x32 bf16 MFMA (K_tile
-//        rows are the A operand straight from LDS; Q stays in 72 VGPRs),
-//   online softmax in the base-2 domain; the row max is shared by the four
-//        lanes holding a head (permlane16 + permlane32 swaps); lazy rescale:
-//        the exponent offset only moves when a new maximum exceeds it by more
-//        than 8 (so P <= 2^8),
-//   O (16 heads x d_c) += P . V_tile                  on 16x16x32 bf16 MFMA; P
-//        leaves the S^T accumulator already in A-operand order and V_tile is
-//        read with the LDS transpose read.  O lives in 128 accumulator registers.
+// k_split design (gfx950): one workgroup of NW waves holds every head of one
+// sequence piece (NW = 8 for up to 128 heads), so each 32-token tile of
+// 576-element rows is fetched from HBM once and shared by all heads.  Tiles
+// are gathered page by page with direct global->LDS 16-byte copies into a ring
+// of NBUF buffers (two tiles in flight while two are in use); 16-byte chunks
+// are XOR-swizzled within 1 KB blocks of 8 rows so that the row-strided MFMA
+// operand reads spread over the LDS banks.  One barrier per tile: step it
+// computes S(it) = K_tile . Q^T and its softmax, publishes P(it) (bf16, PV
+// A-operand order) to a double-buffered LDS slot, and accumulates
+// O += P(it - 1) . V_tile(it - 1) on 16x16x32 bf16 MFMAs with V read by the
+// LDS transpose read.  The softmax is base-2 with a per-head exponent offset
+// fixed by the piece's first tile; a piece whose scores later exceed it by
+// more than kHeadroom is recomputed once with the true maxima.
+//   General layout: every wave scores 16 heads (Q in 72 VGPRs; the head's row
+//        max is shared by four lanes) and accumulates O for all heads over
+//        its d_c / NW columns (128 accumulator registers at d_c 512).
+//   Specialised layout (d_c 512, d_rope 64, NW 8, bf16 cache): waves 0-3
+//        score 32 heads each, every K operand read feeding the MFMAs of two
+//        16-head groups (Q in 144 VGPRs, four independent accumulator
+//        chains), and accumulate O for 2 column blocks; waves 4-7 accumulate
+//        O for 6 column blocks each and issue all tile copies, so the
+//        copies' issue stalls never hold up the scoring waves.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -60,16 +66,16 @@ constexpr float kHeadroom = 64.0f;  // log2 units
 #endif
 constexpr int kQkAhead = MLA_QK_AHEAD;
 constexpr int kPvAhead = MLA_PV_AHEAD;
-// specialised path: K operand reads in flight ahead of the 32x32x16 MFMAs, and
+// specialised path: K operand reads in flight ahead of their MFMA pairs, and
 // whether the loader waves issue a tile's copies after their PV instead of
 // right after the barrier
-#ifndef MLA_QK32_AHEAD
-#define MLA_QK32_AHEAD 2
+#ifndef MLA_QK2_AHEAD
+#define MLA_QK2_AHEAD 2
 #endif
 #ifndef MLA_SPEC_LATE_ISSUE
 #define MLA_SPEC_LATE_ISSUE 0
 #endif
-constexpr int kQk32Ahead = MLA_QK32_AHEAD;
+constexpr int kQk2Ahead = MLA_QK2_AHEAD;
 constexpr bool kSpecLateIssue = MLA_SPEC_LATE_ISSUE != 0;
 #ifndef MLA_SPEC_QK_PRIO
 #define MLA_SPEC_QK_PRIO 0
@@ -91,9 +97,9 @@ struct DecodeCfg {
   static constexpr int THREADS = 64 * NW;
   // tile loads are issued by the last LW waves (the others start computing
   // right after each barrier); loader i issues blocks i, i + LW, ...
-  // Specialised V3-shaped layout (d_c 512, d_rope 64, 8 waves, bf16 cache):
-  // waves 0-3 score 32 heads each on 32x32x16 MFMAs, waves 4-7 only
-  // accumulate O and issue the tile loads.
+  // Specialised layout (d_c 512, d_rope 64, 8 waves, bf16 cache): waves 0-3
+  // score 32 heads each, waves 4-7 accumulate most of O and issue every tile
+  // copy (loader i copies the tile's 8-row group i).
   static constexpr bool SPEC = NW == 8 && DC == 512 && DR == 64 && !FP8;
   static constexpr int LW = SPEC ? 4
                             : (MLA_LOADER_WAVES > 0 && MLA_LOADER_WAVES < NW) ? MLA_LOADER_WAVES : NW;
@@ -523,14 +529,14 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     };
 
     if constexpr (Cfg::SPEC) {
-    // ---- Specialised roles.  QK waves (0-3): S^T (32 tokens x 32 heads) on
-    // 32x32x16 MFMAs with the K tile as the A operand from LDS and Q (32 heads
-    // x 576) in 144 VGPRs, softmax, P published to LDS, and O for column
-    // blocks [2w, 2w + 2).  PV waves (4-7): O for column blocks
-    // [8 + 6(w - 4), +6), and every tile load.  One barrier per tile as in the
-    // general path: step it computes S(it) and PV(it - 1).
+    // ---- Specialised roles.  QK waves (0-3): S^T (32 tokens x 32 heads) as
+    // two 16-head groups sharing every K operand read (K tile rows are the A
+    // operand from LDS; Q of 32 heads x 576 in 144 VGPRs), softmax, P
+    // published to LDS, and O for column blocks [2w, 2w + 2).  PV waves
+    // (4-7): O for column blocks [8 + 6(w - 4), +6), and every tile copy.  One
+    // barrier per tile as in the general path: step it computes S(it) and
+    // PV(it - 1).
     constexpr int QH = 32, NQW = 4, QCB = 2, PCB = 6;
-    constexpr int KS = R / 16;                    // 16-wide k-steps
     constexpr int AHEAD = Cfg::NBUF - 2;
     static_assert(NQW * QH == 16 * NW && NQW * QCB + (NW - NQW) * PCB == Cfg::VCB && Cfg::BLOCKED &&
                   Cfg::LW == NW - NQW && Cfg::INSTR % Cfg::LW == 0 && AHEAD >= 1, "specialised shape");
@@ -664,7 +670,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
                                                  1024 * (kc >> 1));
         };
         constexpr int NQ = 2 * Cfg::K32;
-        constexpr int QD = kQk32Ahead;
+        constexpr int QD = kQk2Ahead;
         f32x4 sacc[2][2] = {};
         bf16x8 abuf[QD];
 #pragma unroll
