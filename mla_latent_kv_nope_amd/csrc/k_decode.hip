@@ -42,6 +42,8 @@
 //        chains), and accumulate O for 2 column blocks; waves 4-7 accumulate
 //        O for 6 column blocks each and issue all tile copies, so the
 //        copies' issue stalls never hold up the scoring waves.
+#include <type_traits>
+
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -300,10 +302,11 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   const bool hi_loader = loader >= 0 && (REM == 0 || loader < REM);
   const bool lo_loader = loader >= 0 && !hi_loader;
 
-  // rows that are skipped keep whatever the buffer held; start from zeros so it is finite
-  for (int i = threadIdx.x; i < Cfg::NBUF * Cfg::TILE_BYTES / 16; i += Cfg::THREADS)
-    reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
+  // The tile ring needs no initialisation: every row of every tile that is
+  // read is copied first (a row past the sequence end copies the tile's first
+  // row, a real token; a row whose page id lies outside the pool copies from
+  // inside the pool), and ring slots beyond a piece's tile count are never
+  // read.
 
 
   // Per-lane LDS byte offsets (relative to a tile buffer) of the MFMA operand
@@ -655,64 +658,78 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       }
       f32x4 oo[NW][QCB];
       float m_use[2] = {-INFINITY, -INFINITY};   // exponent offset per head group (set by the first tile)
-      float m_seen[2] = {-INFINITY, -INFINITY};  // running maxima
+      // this lane's largest exponent argument (score . scale_log2 - offset)
+      // since the offset was set: the overflow test and, for a recompute, the
+      // true maximum, with no cross-lane reduction per tile
+      float y_max[2] = {-INFINITY, -INFINITY};
       float l_part[2] = {0.f, 0.f};              // this lane's shares of the denominators
-      bool overflow = false;
       // S^T (32 tokens x 32 heads) of one tile as four 16x16 accumulator
       // chains (token block x head group): each K operand read (row 16tbk +
       // l16, 16-byte chunk 4kc + quad) feeds the MFMAs of both head groups.
-      // Then the softmax of each group and P to slot pslot.
+      // Then the softmax of each group and P to slot pslot.  A tile that runs
+      // past the sequence end is a separate copy of the body (MASK), so the
+      // steady-state tiles carry no masking.
       auto score2 = [&](const char* tb, int tok0, bool set_offset, int pslot) {
-        const QkBases qb = qk_bases();
-        auto a_ptr = [&](int i) {
-          const int kc = i >> 1, tbk = i & 1;
-          return reinterpret_cast<const bf16x8*>(tb + ((kc & 1) ? qb.odd : qb.even) + tbk * 16 * ROWB +
-                                                 1024 * (kc >> 1));
-        };
-        constexpr int NQ = 2 * Cfg::K32;
-        constexpr int QD = kQk2Ahead;
-        f32x4 sacc[2][2] = {};
-        bf16x8 abuf[QD];
+        auto body = [&](auto mask_t) {
+          constexpr bool MASK = decltype(mask_t)::value;
+          const QkBases qb = qk_bases();
+          auto a_ptr = [&](int i) {
+            const int kc = i >> 1, tbk = i & 1;
+            return reinterpret_cast<const bf16x8*>(tb + ((kc & 1) ? qb.odd : qb.even) + tbk * 16 * ROWB +
+                                                   1024 * (kc >> 1));
+          };
+          constexpr int NQ = 2 * Cfg::K32;
+          constexpr int QD = kQk2Ahead;
+          f32x4 sacc[2][2] = {};
+          bf16x8 abuf[QD];
 #pragma unroll
-        for (int i = 0; i < QD; ++i) abuf[i] = *a_ptr(i);
+          for (int i = 0; i < QD; ++i) abuf[i] = *a_ptr(i);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          const bf16x8 av = abuf[i % QD];
-          if (i + QD < NQ) abuf[i % QD] = *a_ptr(i + QD);
-          sacc[0][i & 1] = mfma16(av, qg[0][i >> 1], sacc[0][i & 1]);
-          sacc[1][i & 1] = mfma16(av, qg[1][i >> 1], sacc[1][i & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // sacc[g][tbk][i] is token 16tbk + 4quad + i of head hq + 16g + l16
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          float x[8];
-          float mt = -INFINITY;
-#pragma unroll
-          for (int tbk = 0; tbk < 2; ++tbk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = 16 * tbk + 4 * quad + i;
-              const float v = (tok0 + kTile <= S || tok0 + t < S) ? sacc[g][tbk][i] : -INFINITY;
-              x[4 * tbk + i] = v;
-              mt = fmaxf(mt, v);
-            }
-          mt = max_across_half_waves(max_across_quarter_pairs(mt)) * a.scale_log2;
-          m_seen[g] = fmaxf(m_seen[g], mt);
-          if (set_offset) m_use[g] = mt;            // first tile: O is still zero
-          overflow |= mt > m_use[g] + kHeadroom;
-          uint32_t pu[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j], a.scale_log2, -m_use[g]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j + 1], a.scale_log2, -m_use[g]));
-            l_part[g] += p0 + p1;
-            pu[j] = pack_bf16x2(p0, p1);
+          for (int i = 0; i < NQ; ++i) {
+            const bf16x8 av = abuf[i % QD];
+            if (i + QD < NQ) abuf[i % QD] = *a_ptr(i + QD);
+            sacc[0][i & 1] = mfma16(av, qg[0][i >> 1], sacc[0][i & 1]);
+            sacc[1][i & 1] = mfma16(av, qg[1][i >> 1], sacc[1][i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          // P in PV A-operand order: k slot 8quad + j <-> token (j < 4 ? 4quad + j : 16 + 4quad + j - 4)
-          *reinterpret_cast<bf16x8*>(pbuf + pslot * PSLOT + (hq + 16 * g) * PROW + p_lane_off()) =
-              __builtin_bit_cast(bf16x8, pu);
-        }
+          const uint32_t poff = p_lane_off();
+          // sacc[g][tbk][i] is token 16tbk + 4quad + i of head hq + 16g + l16
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            float x[8];
+#pragma unroll
+            for (int tbk = 0; tbk < 2; ++tbk)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tbk + 4 * quad + i;
+                x[4 * tbk + i] = (!MASK || tok0 + t < S) ? sacc[g][tbk][i] : -INFINITY;
+              }
+            if (set_offset) {                       // first tile: O is still zero
+              float mt = -INFINITY;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) mt = fmaxf(mt, x[i]);
+              m_use[g] = max_across_half_waves(max_across_quarter_pairs(mt)) * a.scale_log2;
+            }
+            uint32_t pu[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float y0 = fmaf(x[2 * j], a.scale_log2, -m_use[g]);
+              const float y1 = fmaf(x[2 * j + 1], a.scale_log2, -m_use[g]);
+              y_max[g] = fmaxf(y_max[g], fmaxf(y0, y1));
+              const float p0 = __builtin_amdgcn_exp2f(y0);
+              const float p1 = __builtin_amdgcn_exp2f(y1);
+              l_part[g] += p0 + p1;
+              pu[j] = pack_bf16x2(p0, p1);
+            }
+            // P in PV A-operand order: k slot 8quad + j <-> token (j < 4 ? 4quad + j : 16 + 4quad + j - 4)
+            *reinterpret_cast<bf16x8*>(pbuf + pslot * PSLOT + (hq + 16 * g) * PROW + poff) =
+                __builtin_bit_cast(bf16x8, pu);
+          }
+        };
+        if (tok0 + kTile <= S)
+          body(std::false_type{});
+        else
+          body(std::true_type{});
       };
 
       for (int pass = 0;; ++pass) {
@@ -721,7 +738,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
 #pragma unroll
           for (int c = 0; c < QCB; ++c) oo[hb][c] = f32x4{};
         l_part[0] = l_part[1] = 0.f;
-        overflow = false;
+        y_max[0] = y_max[1] = -INFINITY;
         sync_tile(0);
         score2(lds, lt0 * kTile, pass == 0, 0);
         for (int it = 1; it < ntiles; ++it) {
@@ -731,10 +748,11 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         }
         block_barrier();
         pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1, QCB * wave, oo);
-        const bool again = vote_again(overflow);
+        const bool again = vote_again(y_max[0] > kHeadroom || y_max[1] > kHeadroom);
         if (!again || pass > 0) break;   // the second pass starts at the true maximum
-        m_use[0] = m_seen[0];
-        m_use[1] = m_seen[1];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          m_use[g] += max_across_half_waves(max_across_quarter_pairs(y_max[g]));
       }
       // 1/l and lse of this wave's heads (four lanes hold a head)
 #pragma unroll
