@@ -176,6 +176,40 @@ mla_status_t mla_decode_paged(const mla_dims_t* dims, const void* q, const void*
                               int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
                               float* lse, void* stream);
 
+/* Largest q_len mla_decode_paged_multi accepts. */
+#define MLA_MAX_Q_LEN 16
+
+/*
+ * mla_decode_paged_multi - mla_decode_paged for q_len new tokens per sequence
+ * in one pass, each attending causally: the verification pass of speculative
+ * decoding with multi-token-prediction drafts.
+ * Source: draft tokens from the multi-token-prediction layers are verified by
+ * the main model in one parallel pass (deepseek.csdn.net section 6;
+ * agent.csdn.net section 5.3, item 3); each query is the absorbed MLA decode
+ * query above.  Reading: the q_len new tokens are already appended, as the
+ * last q_len tokens of each sequence, and new token i (0-based) sees the
+ * context and new tokens 0..i.
+ *
+ *   q           bf16 [B][q_len][H][d_c + d_rope] from mla_absorb_q called on
+ *               B * q_len rows with positions seq_lens[b] - q_len + i
+ *   q_len       1 .. MLA_MAX_Q_LEN (1 is exactly mla_decode_paged)
+ *   seq_lens    int32 [B]: tokens of each sequence including its q_len new
+ *               ones; new token i sees its first seq_lens[b] - (q_len - 1 - i)
+ *               tokens (none if that is <= 0: o_lat = 0, lse = -inf)
+ *   workspace   at least mla_decode_workspace_size(dims, B * q_len, num_splits)
+ *               bytes
+ *   o_lat       bf16 [B][q_len][H][d_c] (written), lse fp32 [B][q_len][H] or NULL
+ * Other arguments, errors and results as for mla_decode_paged; q_len outside
+ * 1 .. MLA_MAX_Q_LEN is MLA_ERR_INVALID_ARG.  The workgroups of the q_len
+ * new tokens of a sequence are placed side by side on one XCD, where their
+ * reads of the same pages can share that XCD's L2.
+ */
+mla_status_t mla_decode_paged_multi(const mla_dims_t* dims, const void* q, const void* pool,
+                                    const float* scales, const int32_t* block_table,
+                                    int32_t max_pages, int32_t num_pages, const int32_t* seq_lens,
+                                    int32_t B, int32_t q_len, int32_t num_splits, void* workspace,
+                                    size_t ws_bytes, void* o_lat, float* lse, void* stream);
+
 /*
  * mla_out_proj - apply W_UV on the output side.
  * Source: W_UV is absorbed into the output projection (sheratonhq.com section 2.1).

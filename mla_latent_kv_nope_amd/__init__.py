@@ -7,7 +7,7 @@ library is missing; `mla_latent_kv_nope_amd.build` builds it.
 """
 _API = (
     "Dims", "LIB_PATH", "MlaError", "absorb_q", "append_latent", "cache_bytes_per_token",
-    "decode_paged", "decode_workspace_size", "make_dims", "new_pool", "new_workspace", "out_proj",
+    "decode_paged", "decode_paged_multi", "decode_workspace_size", "make_dims", "new_pool", "new_workspace", "out_proj",
     "pool_shape", "profile_begin", "profile_end", "status_string",
 )
 __all__ = list(_API)

@@ -41,9 +41,11 @@ MLA_ERR_HIP = 4
 MLA_CACHE_BF16 = 0
 MLA_CACHE_FP8_E4M3 = 1
 MLA_APPEND_NO_ROPE = 1
+MLA_MAX_Q_LEN = 16
 
 EXPORTS = (
     "mla_append_latent", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_paged",
+    "mla_decode_paged_multi",
     "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_last_hip_error",
     "mla_profile_begin", "mla_profile_end",
 )
@@ -69,6 +71,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, ctypes.c_size_t,
                                      _P, _P, _P]
     lib.mla_decode_paged.restype = ctypes.c_int
+    lib.mla_decode_paged_multi.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P,
+                                           ctypes.c_size_t, _P, _P, _P]
+    lib.mla_decode_paged_multi.restype = ctypes.c_int
     lib.mla_out_proj.argtypes = [_DP, _P, _P, _I, _P, _P]
     lib.mla_out_proj.restype = ctypes.c_int
     lib.mla_cache_bytes_per_token.argtypes = [_DP]

@@ -171,6 +171,45 @@ def decode_paged(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Optional[
     return o_lat, lse
 
 
+def decode_paged_multi(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Optional[torch.Tensor],
+                       block_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int = 0,
+                       workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """mla_decode_paged_multi: q is [B][q_len][H][R]; returns o_lat [B][q_len][H][d_c]
+    and lse [B][q_len][H] (or None)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][q_len][H][d_c + d_rope]")
+    B, q_len = q.shape[0], q.shape[1]
+    H, R = d.n_heads, d.d_c + d.d_rope
+    _req(q, "q", torch.bfloat16, (B, q_len, H, R))
+    num_pages = pool.shape[0]
+    if _is_fp8(d):
+        _req(pool, "pool", torch.uint8, pool_shape(d, num_pages))
+        _req(scales, "scales", torch.float32, (num_pages, d.page_size))
+    else:
+        _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages]")
+    _req(block_table, "block_table", torch.int32)
+    _req(seq_lens, "seq_lens", torch.int32, (B,))
+    if workspace is None:
+        workspace = new_workspace(d, B * q_len, num_splits, q.device)
+    _req(workspace, "workspace", torch.uint8)
+    if o_lat is None:
+        o_lat = torch.empty((B, q_len, H, d.d_c), dtype=torch.bfloat16, device=q.device)
+    _req(o_lat, "o_lat", torch.bfloat16, (B, q_len, H, d.d_c))
+    if lse is None and want_lse:
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _req(lse, "lse", torch.float32, (B, q_len, H))
+    st = lib.mla_decode_paged_multi(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales),
+                                    _ptr(block_table), block_table.shape[1], num_pages,
+                                    _ptr(seq_lens), B, int(q_len), int(num_splits), _ptr(workspace),
+                                    workspace.numel(), _ptr(o_lat), _ptr(lse), _stream())
+    _check("mla_decode_paged_multi", st)
+    return o_lat, lse
+
+
 def out_proj(d: Dims, o_lat: torch.Tensor, w_uv: torch.Tensor,
              out: Optional[torch.Tensor] = None) -> torch.Tensor:
     B = o_lat.shape[0]

@@ -235,7 +235,15 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   // C consecutive sequences; a wave scan plus the wave totals (in the P slots,
   // unused until the first tile) give each chunk's first tile.  Workgroup 0
   // also stores the prefix sums and the quota for k_combine.
-  auto tiles_of = [&](int bb) { return (clamp_len(seq_lens[bb], cap) + kTile - 1) / kTile; };
+  // tokens seen by query sequence bb (its cache sequence's length, less the
+  // later new tokens of the same sequence when q_len > 1)
+  const int QL = a.q_len;
+  auto seq_len_of = [&](int bb) {
+    if (QL == 1) return clamp_len(seq_lens[bb], cap);
+    const int cs = bb / QL;
+    return clamp_len(seq_lens[cs] - (QL - 1 - (bb - cs * QL)), cap);
+  };
+  auto tiles_of = [&](int bb) { return (seq_len_of(bb) + kTile - 1) / kTile; };
   int* const scan = reinterpret_cast<int*>(pbuf);
   const int C = (B + Cfg::THREADS - 1) / Cfg::THREADS;
   const int k0 = static_cast<int>(threadIdx.x) * C;
@@ -360,9 +368,9 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     const int t1 = t0 + tiles_of(b);
     const int lt0 = g - t0, lt1 = min(gend, t1) - t0;
     const int ntiles = lt1 - lt0;
-    const int S = clamp_len(seq_lens[b], cap);
+    const int S = seq_len_of(b);
     const bool whole = (lt0 == 0) && (lt1 == t1 - t0);
-    const int32_t* bt = block_table + static_cast<int64_t>(b) * a.max_pages;
+    const int32_t* bt = block_table + static_cast<int64_t>(QL == 1 ? b : b / QL) * a.max_pages;
     const char* pool = static_cast<const char*>(a.pool);
     const int64_t page_bytes = static_cast<int64_t>(ROWB) << lg;
 

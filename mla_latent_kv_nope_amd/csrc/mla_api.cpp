@@ -156,14 +156,19 @@ size_t mla_decode_workspace_size(const mla_dims_t* d, int32_t B, int32_t num_spl
   return mla::decode_workspace_layout(B, d->n_heads, d->d_c, parts).total;
 }
 
-mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* pool,
-                              const float* scales, const int32_t* block_table, int32_t max_pages,
-                              int32_t num_pages, const int32_t* seq_lens, int32_t B,
-                              int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
-                              float* lse, void* stream) {
+namespace {
+
+// Both decode entry points: q_len new tokens per cache sequence (1 = plain
+// decode), run as B * q_len query sequences.
+mla_status_t decode_impl(const mla_dims_t* d, const void* q, const void* pool, const float* scales,
+                         const int32_t* block_table, int32_t max_pages, int32_t num_pages,
+                         const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t num_splits,
+                         void* workspace, size_t ws_bytes, void* o_lat, float* lse, void* stream) {
   const mla_status_t st = check_dims(d);
   if (st != MLA_OK) return st;
   if (B <= 0 || max_pages <= 0 || num_pages <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
+  if (q_len < 1 || q_len > MLA_MAX_Q_LEN || static_cast<int64_t>(B) * q_len > (int64_t{1} << 24))
+    return MLA_ERR_INVALID_ARG;
   if (!q || !pool || !block_table || !seq_lens || !workspace || !o_lat) return MLA_ERR_INVALID_ARG;
   const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
   if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
@@ -173,12 +178,14 @@ mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* po
     return MLA_ERR_INVALID_ARG;
   if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads, fp8)) return MLA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_UNSUPPORTED;
-  const int parts = effective_parts(num_splits, B, d->n_heads);
-  const mla::WorkspaceLayout L = mla::decode_workspace_layout(B, d->n_heads, d->d_c, parts);
+  const int BQ = B * q_len;                     // query sequences
+  const int parts = effective_parts(num_splits, BQ, d->n_heads);
+  const mla::WorkspaceLayout L = mla::decode_workspace_layout(BQ, d->n_heads, d->d_c, parts);
   if (ws_bytes < L.total) return MLA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   mla::DecodeArgs a{};
-  a.B = B;
+  a.B = BQ;
+  a.q_len = q_len;
   a.H = d->n_heads;
   a.d_c = d->d_c;
   a.d_rope = d->d_rope;
@@ -205,6 +212,26 @@ mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* po
     ++g_prof.used;
   }
   return from_hip(mla::launch_decode(a, static_cast<hipStream_t>(stream), e0, e1));
+}
+
+}  // namespace
+
+mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* pool,
+                              const float* scales, const int32_t* block_table, int32_t max_pages,
+                              int32_t num_pages, const int32_t* seq_lens, int32_t B,
+                              int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
+                              float* lse, void* stream) {
+  return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, 1, num_splits,
+                     workspace, ws_bytes, o_lat, lse, stream);
+}
+
+mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const void* pool,
+                                    const float* scales, const int32_t* block_table, int32_t max_pages,
+                                    int32_t num_pages, const int32_t* seq_lens, int32_t B, int32_t q_len,
+                                    int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
+                                    float* lse, void* stream) {
+  return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
+                     num_splits, workspace, ws_bytes, o_lat, lse, stream);
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* d, const void* o_lat, const void* w_uv, int32_t B,

@@ -51,8 +51,15 @@ struct OutProjArgs {
 //             outputs in the decode waves' accumulator order
 //   part_lse  fp32 [num_parts + B][H]
 // A partial computed by workgroup w for sequence b lives in slot w + b.
+//
+// With q_len > 1 (several new tokens per sequence, scored in one pass), the
+// kernels work on B = (cache sequences) x q_len query sequences: query
+// sequence v is token i = v % q_len of cache sequence v / q_len, reads that
+// sequence's block-table row and sees its first seq_lens[v / q_len] -
+// (q_len - 1 - i) tokens (causal among the new tokens).  q_len = 1 is
+// single-token decode.
 struct DecodeArgs {
-  int B, H, d_c, d_rope, page_size_log2, max_pages, num_pages, num_parts;
+  int B, H, d_c, d_rope, page_size_log2, max_pages, num_pages, num_parts, q_len;
   bool fp8;
   float scale_log2;  // softmax_scale * log2(e)
   const uint16_t* q;

@@ -252,3 +252,36 @@ def reference_decode(inp, batches=None, heads=None):
                                    wl.softmax_scale, wl.rope_base, heads)
         out[i], lse[i], o_lat[i] = o, l, ol
     return {"out": out, "lse": lse, "o_lat": o_lat}
+
+
+def reference_decode_multi(inp, batches=None, heads=None):
+    """Explicit-form oracle for q_len > 1 new tokens per sequence, scored in one
+    pass (the verification of multi-token-prediction drafts: "deepseek.csdn.net"
+    section 6).  Reading: the q_len new tokens are the last q_len cached tokens
+    of each sequence, and new token i (0-based) attends causally, to the first
+    L = S_b - q_len + 1 + i tokens, from position L - 1.  Each query is
+    `decode_explicit` over that prefix.
+
+    Returns dict with out [nb][q_len][nh][d_v], lse [nb][q_len][nh] and
+    o_lat [nb][q_len][nh][d_c]."""
+    wl = inp.wl
+    ql = wl.q_len
+    B, H = len(inp.seq_lens), wl.n_heads
+    batches = list(range(B)) if batches is None else list(batches)
+    heads = list(range(H)) if heads is None else list(heads)
+    w_uk = bf16_bits_to_f64(inp.w_uk)
+    w_uv = bf16_bits_to_f64(inp.w_uv)
+    out = np.zeros((len(batches), ql, len(heads), wl.d_v))
+    o_lat = np.zeros((len(batches), ql, len(heads), wl.d_c))
+    lse = np.zeros((len(batches), ql, len(heads)))
+    for n, b in enumerate(batches):
+        C, Kr = sequence_rows(inp, b)
+        S = int(inp.seq_lens[b])
+        qn = bf16_bits_to_f64(inp.q_nope[b]).reshape(ql, H, wl.d_nope)
+        qp = bf16_bits_to_f64(inp.q_pe[b]).reshape(ql, H, wl.d_rope)
+        for i in range(ql):
+            L = max(0, S - ql + 1 + i)
+            o, l, ol = decode_explicit(qn[i], qp[i], C[:L], Kr[:L], w_uk, w_uv, L - 1,
+                                       wl.softmax_scale, wl.rope_base, heads)
+            out[n, i], lse[n, i], o_lat[n, i] = o, l, ol
+    return {"out": out, "lse": lse, "o_lat": o_lat}

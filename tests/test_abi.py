@@ -141,6 +141,25 @@ def test_decode_validation():
     _expect(call(maxp=0), _native.MLA_ERR_INVALID_ARG)
 
 
+def test_decode_multi_validation():
+    """mla_decode_paged_multi: q_len range, and a workspace sized for B * q_len
+    query sequences."""
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    f = lib.mla_decode_paged_multi
+    B, ql = 4, 3
+    need = lib.mla_decode_workspace_size(ctypes.byref(d), B * ql, 0)
+    assert need > lib.mla_decode_workspace_size(ctypes.byref(d), B, 0)
+
+    def call(q_len=ql, wsb=need, q=P):
+        return f(ctypes.byref(d), q, P, None, P, 8, 40, P, B, q_len, 0, P, wsb, P, P, None)
+
+    for bad in (0, -1, _native.MLA_MAX_Q_LEN + 1):
+        _expect(call(q_len=bad), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(wsb=need - 1), _native.MLA_ERR_WORKSPACE)
+    _expect(call(q=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(q=P + 8), _native.MLA_ERR_INVALID_ARG)          # q not 16-byte aligned
+
+
 def test_binding_rejects_host_tensors():
     import torch
     d = mla.make_dims(4, 32, 16, 16, 16, 16)

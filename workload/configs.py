@@ -31,6 +31,9 @@ class Workload:
     seq_len: Optional[int] = None
     seq_range: Optional[tuple] = None
     fp8: bool = False
+    # new tokens per sequence scored in one pass (speculative verification of
+    # multi-token-prediction drafts); they are the last q_len cached tokens
+    q_len: int = 1
     rope_base: float = 10000.0
     spare_pages: int = 3
     seed: int = 0
@@ -84,7 +87,14 @@ FP8LONG = Workload(
     page_size=64, seq_len=131072, fp8=True,
     description="Long context: B=4 H=128 S=131072 page 64, fp8 e4m3 cache + per-token fp32 scale")
 
-ALL = {w.name: w for w in (TINY, V2LITE, V3, RAGGED, FP8LONG)}
+# Multi-token query: the verification pass over q_len draft tokens per
+# sequence ("deepseek.csdn.net" section 6: drafts from the multi-token-prediction
+# layers verified by the main model in one parallel pass, e.g. 4 drafts;
+# agent.csdn.net section 5.3: the first two or three drafts are usually kept).
+V3_MTP2 = V3.with_(name="v3mtp2", q_len=2,
+                   description="DeepSeek-V3-shaped verification pass: B=64 q_len=2 H=128 S=8192 page 64, bf16")
+
+ALL = {w.name: w for w in (TINY, V2LITE, V3, RAGGED, FP8LONG, V3_MTP2)}
 
 
 def get(name: str) -> Workload:

@@ -41,8 +41,8 @@ class DecodeInputs:
     cu_seqlens: np.ndarray    # int64 [B+1], token offsets into c_kv / k_pe
     block_table: np.ndarray   # int32 [B][max_pages]; -1 = unused entry
     num_pages: int            # physical pages in the pool (includes spares)
-    q_nope: np.ndarray        # uint16 bf16 bits [B][H][d_nope]
-    q_pe: np.ndarray          # uint16 bf16 bits [B][H][d_rope]   (un-rotated)
+    q_nope: np.ndarray        # uint16 bf16 bits [B][H][d_nope]  ([B][q_len][H][d_nope] if q_len > 1)
+    q_pe: np.ndarray          # uint16 bf16 bits [B][H][d_rope]  (likewise; un-rotated)
     c_kv: np.ndarray          # uint16 bf16 bits [T][d_c]          (sequence-major)
     k_pe: np.ndarray          # uint16 bf16 bits [T][d_rope]       (un-rotated)
     w_uk: np.ndarray          # uint16 bf16 bits [H][d_c][d_nope]
@@ -66,8 +66,13 @@ class DecodeInputs:
         return np.repeat(np.arange(len(self.seq_lens), dtype=np.int32), self.seq_lens)
 
     def q_pos(self) -> np.ndarray:
-        """Query position: the current token is the last cached one."""
-        return (self.seq_lens - 1).astype(np.int32)
+        """Query position: the current token is the last cached one (int32 [B]);
+        with q_len > 1 new tokens, they are the last q_len cached ones
+        (int32 [B][q_len], position seq_len - q_len + i)."""
+        ql = self.wl.q_len
+        if ql == 1:
+            return (self.seq_lens - 1).astype(np.int32)
+        return (self.seq_lens[:, None] - ql + np.arange(ql)[None, :]).astype(np.int32)
 
 
 def _normal_bf16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
@@ -125,8 +130,9 @@ def make_inputs(wl: Workload, seed: int | None = None) -> DecodeInputs:
     cu = np.zeros(B + 1, dtype=np.int64)
     cu[1:] = np.cumsum(seq_lens.astype(np.int64))
     T = int(cu[-1])
-    q_nope = _normal_bf16(rng, (B, H, wl.d_nope), 1.0)
-    q_pe = _normal_bf16(rng, (B, H, wl.d_rope), 1.0)
+    qs = (B, H) if wl.q_len == 1 else (B, wl.q_len, H)
+    q_nope = _normal_bf16(rng, qs + (wl.d_nope,), 1.0)
+    q_pe = _normal_bf16(rng, qs + (wl.d_rope,), 1.0)
     c_kv = _normal_bf16(rng, (T, wl.d_c), 1.0)
     k_pe = _normal_bf16(rng, (T, wl.d_rope), 1.0)
     sw = 1.0 / math.sqrt(wl.d_c)
