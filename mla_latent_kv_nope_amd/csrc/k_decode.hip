@@ -235,21 +235,29 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   // C consecutive sequences; a wave scan plus the wave totals (in the P slots,
   // unused until the first tile) give each chunk's first tile.  Workgroup 0
   // also stores the prefix sums and the quota for k_combine.
-  // tokens seen by query sequence bb (its cache sequence's length, less the
-  // later new tokens of the same sequence when q_len > 1)
+  // Query sequence v is new token qi = v % q_len of cache sequence cs =
+  // v / q_len and sees len_of(cs, qi) tokens (the cache sequence's length less
+  // its later new tokens).  (cs, qi) pairs are walked incrementally: one
+  // division per thread here and one per workgroup for the piece loop.
   const int QL = a.q_len;
-  auto seq_len_of = [&](int bb) {
-    if (QL == 1) return clamp_len(seq_lens[bb], cap);
-    const int cs = bb / QL;
-    return clamp_len(seq_lens[cs] - (QL - 1 - (bb - cs * QL)), cap);
+  auto len_of = [&](int cs, int qi) { return clamp_len(seq_lens[cs] - (QL - 1 - qi), cap); };
+  auto tiles_len = [](int len) { return (len + kTile - 1) / kTile; };
+  auto next_query = [&](int& cs, int& qi) {
+    if (++qi == QL) {
+      qi = 0;
+      ++cs;
+    }
   };
-  auto tiles_of = [&](int bb) { return (seq_len_of(bb) + kTile - 1) / kTile; };
   int* const scan = reinterpret_cast<int*>(pbuf);
   const int C = (B + Cfg::THREADS - 1) / Cfg::THREADS;
   const int k0 = static_cast<int>(threadIdx.x) * C;
+  const int cs0 = k0 / QL, qi0 = k0 - cs0 * QL;   // query sequence k0
   int csum = 0;
-  for (int j = 0; j < C; ++j)
-    if (k0 + j < B) csum += tiles_of(k0 + j);
+  {
+    int cs = cs0, qi = qi0;
+    for (int j = 0; j < C; ++j, next_query(cs, qi))
+      if (k0 + j < B) csum += tiles_len(len_of(cs, qi));
+  }
   int incl = csum;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -268,10 +276,11 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   const int quota = total > 0 ? (total + a.num_parts - 1) / a.num_parts : 1;
   if (w == 0) {
     int p0 = excl;
-    for (int j = 0; j < C; ++j)
+    int cs = cs0, qi = qi0;
+    for (int j = 0; j < C; ++j, next_query(cs, qi))
       if (k0 + j < B) {
         plan[k0 + j] = p0;
-        p0 += tiles_of(k0 + j);
+        p0 += tiles_len(len_of(cs, qi));
       }
     if (threadIdx.x == 0) {
       plan[B] = total;
@@ -285,8 +294,9 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   // the chunk holding tile g names the sequence containing it
   if (excl <= g && g < excl + csum) {
     int p0 = excl;
-    for (int j = 0; j < C; ++j) {
-      const int n = k0 + j < B ? tiles_of(k0 + j) : 0;
+    int cs = cs0, qi = qi0;
+    for (int j = 0; j < C; ++j, next_query(cs, qi)) {
+      const int n = k0 + j < B ? tiles_len(len_of(cs, qi)) : 0;
       if (g < p0 + n) {
         scan[0] = k0 + j;
         scan[1] = p0;
@@ -298,6 +308,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   __syncthreads();
   int b = scan[0];
   int t0 = scan[1];                             // first tile of sequence b
+  int b_cs = b / QL, b_qi = b - b_cs * QL;      // its cache sequence and new-token index
   const int quad = lane >> 4;          // k slice (operands) / token quad (S) / head quad (O)
   const int l16 = lane & 15;
   const int lg = a.page_size_log2;
@@ -365,12 +376,12 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   };
 
   while (g < gend) {
-    const int t1 = t0 + tiles_of(b);
+    const int S = len_of(b_cs, b_qi);
+    const int t1 = t0 + tiles_len(S);
     const int lt0 = g - t0, lt1 = min(gend, t1) - t0;
     const int ntiles = lt1 - lt0;
-    const int S = seq_len_of(b);
     const bool whole = (lt0 == 0) && (lt1 == t1 - t0);
-    const int32_t* bt = block_table + static_cast<int64_t>(QL == 1 ? b : b / QL) * a.max_pages;
+    const int32_t* bt = block_table + static_cast<int64_t>(b_cs) * a.max_pages;
     const char* pool = static_cast<const char*>(a.pool);
     const int64_t page_bytes = static_cast<int64_t>(ROWB) << lg;
 
@@ -1145,7 +1156,11 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     g = t0 + lt1;
     t0 = t1;
     ++b;
-    while (b < B && tiles_of(b) == 0) ++b;
+    next_query(b_cs, b_qi);
+    while (b < B && len_of(b_cs, b_qi) == 0) {
+      ++b;
+      next_query(b_cs, b_qi);
+    }
     // all waves must be done reading the ring and the shared 1/l before the
     // next piece refills them
     __syncthreads();
