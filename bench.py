@@ -10,6 +10,10 @@ inputs resident in HBM.  The cache holds S-1 tokens per sequence before the
 timed region; every step appends token S-1 (the same slot each step) and
 attends over all S tokens.
 
+`--workload v3mtp2` runs the same step for two new tokens per sequence scored
+in one pass (mla_decode_paged_multi; the verification of multi-token-prediction
+drafts); its tokens/s counts the B * q_len scored tokens.
+
 Prints one JSON line: whole-step decode tokens/s, plus
   roofline: the split-attention kernel's achieved HBM bandwidth
             (algorithmic bytes per launch / its mean duration, HIP events on
@@ -37,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="v3", choices=["v3", "v2lite", "ragged", "fp8long"])
+    ap.add_argument("--workload", default="v3", choices=["v3", "v2lite", "ragged", "fp8long", "v3mtp2"])
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=24,
                     help="sequences of the workload the oracle decodes for cpu_baseline (0 = skip)")
@@ -69,7 +73,10 @@ def measured_traffic(workload: str):
     the workload differs."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "k_split_v3_b64_s8192.md")
+    name = {"v3": "k_split_v3_b64_s8192.md", "v3mtp2": "k_split_v3mtp2_b64_q2_s8192.md"}.get(workload)
+    if name is None:
+        return None
+    path = os.path.join(ROOT, "profiles", name)
     try:
         text = open(path, encoding="utf-8").read()
         block = json.loads(re.search(r"```json\n(.*?)```", text, re.S).group(1))
@@ -90,19 +97,23 @@ def measured_traffic(workload: str):
 def cpu_baseline(inp, n_seq: int):
     """Time the oracle (explicit fp64 form) on the first n_seq sequences."""
     import numpy as np
-    from oracle import reference_decode
+    from oracle import reference_decode, reference_decode_multi
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    ql = inp.wl.q_len
     t0 = time.perf_counter()
-    reference_decode(inp, batches=range(n_seq))
+    if ql == 1:
+        reference_decode(inp, batches=range(n_seq))
+    else:
+        reference_decode_multi(inp, batches=range(n_seq))
     dt = time.perf_counter() - t0
     toks = int(np.sum(inp.seq_lens[:n_seq]))
-    return {"value": n_seq / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_seq} of {len(inp.seq_lens)} sequences x {inp.wl.n_heads} heads "
-                      f"({toks} cached tokens), explicit fp64 form, {dt:.2f} s",
+    return {"value": n_seq * ql / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_seq} of {len(inp.seq_lens)} sequences x {ql} new token(s) x "
+                      f"{inp.wl.n_heads} heads ({toks} cached tokens), explicit fp64 form, {dt:.2f} s",
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
             "blas": _blas_name()}
 
@@ -178,10 +189,12 @@ def main():
     t = to_device(inp, dev)
     B, H = wl.batch, wl.n_heads
     R = wl.d_c + wl.d_rope
+    ql = wl.q_len
+    BQ = B * ql                       # query rows per step
 
-    # cache: every token but the last of each sequence
+    # cache: every token but the last q_len of each sequence
     cu = inp.cu_seqlens
-    last = (cu[1:] - 1).astype(np.int64)
+    last = (cu[1:, None] - ql + np.arange(ql)[None, :]).reshape(-1).astype(np.int64)
     keep = np.ones(inp.total_tokens, bool)
     keep[last] = False
     idx_keep = torch.from_numpy(np.nonzero(keep)[0]).to(dev)
@@ -196,17 +209,29 @@ def main():
     new_sid = t["seq_ids"][idx_last].contiguous()
     del t["c_kv"], t["k_pe"]
 
-    ws = mla.new_workspace(d, B, args.num_splits, dev)
-    q = torch.empty((B, H, R), dtype=torch.bfloat16, device=dev)
-    o_lat = torch.empty((B, H, wl.d_c), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    out = torch.empty((B, H, wl.d_v), dtype=torch.bfloat16, device=dev)
+    ws = mla.new_workspace(d, BQ, args.num_splits, dev)
+    q = torch.empty((BQ, H, R), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((BQ, H, wl.d_c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((BQ, H), dtype=torch.float32, device=dev)
+    out = torch.empty((BQ, H, wl.d_v), dtype=torch.bfloat16, device=dev)
+    q_nope = t["q_nope"].reshape(BQ, H, wl.d_nope)
+    q_pe = t["q_pe"].reshape(BQ, H, wl.d_rope)
+    q_pos = t["q_pos"].reshape(BQ).contiguous()
+
+    if ql == 1:
+        def decode():
+            mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], args.num_splits,
+                             ws, o_lat, lse)
+    else:
+        def decode():
+            mla.decode_paged_multi(d, q.view(B, ql, H, R), pool, scales, t["block_table"],
+                                   t["seq_lens"], args.num_splits, ws, o_lat.view(B, ql, H, wl.d_c),
+                                   lse.view(B, ql, H))
 
     def step():
         mla.append_latent(d, new_c, new_k, new_pos, new_sid, t["block_table"], pool, scales)
-        mla.absorb_q(d, t["q_nope"], t["q_pe"], t["q_pos"], t["w_uk"], q)
-        mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], args.num_splits,
-                         ws, o_lat, lse)
+        mla.absorb_q(d, q_nope, q_pe, q_pos, t["w_uk"], q)
+        decode()
         mla.out_proj(d, o_lat, t["w_uv"], out)
 
     for _ in range(args.warmup):
@@ -223,28 +248,32 @@ def main():
     assert torch.isfinite(out.float()).all(), "non-finite output"
     flushed = None
     if args.flushed_iters > 0:
-        flushed = flushed_decode_times(
-            mla, torch, lambda: mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"],
-                                                 args.num_splits, ws, o_lat, lse),
-            args.flushed_iters)
+        flushed = flushed_decode_times(mla, torch, decode, args.flushed_iters)
 
     ms_step = 1e3 * elapsed / args.steps
-    value = B * args.steps / elapsed
+    value = BQ * args.steps / elapsed
     total_tokens = int(inp.total_tokens)
     bpt = mla.cache_bytes_per_token(d)
-    split_bytes = total_tokens * bpt + B * H * R * 2          # cache rows + the absorbed query
-    flops = 2.0 * total_tokens * H * (R + wl.d_c)             # QK^T + PV
+    # cache rows (each read once) + the absorbed query rows
+    split_bytes = total_tokens * bpt + BQ * H * R * 2
+    # QK^T + PV over every (query, visible token) pair; new token i of a
+    # sequence sees S - q_len + 1 + i tokens
+    attended = int(np.sum(np.maximum(0, inp.seq_lens[:, None].astype(np.int64) - ql + 1
+                                     + np.arange(ql)[None, :])))
+    flops = 2.0 * attended * H * (R + wl.d_c)
     split_ms = split_ms_total / max(1, n_rec)
     achieved_gbs = split_bytes / (split_ms * 1e-3) / 1e9
     tflops = flops / (split_ms * 1e-3) / 1e12
-    bound = "mfma" if wl.fp8 else "hbm"
+    # the binding roof: HBM time of the bytes vs bf16 MFMA time of the flops
+    bound = "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > split_bytes / (HBM_PEAK_GBS * 1e9) else "hbm"
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(args.workload)}
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.workload)}
     roof.update({"kernel": "k_split (split-KV attention)", "mean_launch_ms": round(split_ms, 5),
                  "launches": n_rec, "algorithmic_bytes_per_launch": split_bytes,
                  "flops_per_launch": flops, "achieved_tflops": round(tflops, 1)})
@@ -255,25 +284,28 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.description, "batch": B, "heads": H, "d_c": wl.d_c,
-                   "d_rope": wl.d_rope, "seq_len": wl.max_seq_len, "total_tokens": total_tokens,
+                   "d_rope": wl.d_rope, "seq_len": wl.max_seq_len, "q_len": ql,
+                   "total_tokens": total_tokens,
                    "page_size": wl.page_size, "cache": "fp8_e4m3" if wl.fp8 else "bf16",
                    "num_splits": args.num_splits or "auto",
-                   "step": "append+absorb+decode(plan,split,combine)+out_proj"},
-        "decode_kernel_tokens_per_s": round(B / (split_ms * 1e-3), 1),
+                   "step": ("append+absorb+decode(plan,split,combine)+out_proj" if ql == 1 else
+                            f"append({ql} new tokens per sequence)+absorb+decode_multi(plan,split,"
+                            f"combine)+out_proj; value counts the B*q_len new tokens scored")},
+        "decode_kernel_tokens_per_s": round(BQ / (split_ms * 1e-3), 1),
         "roofline": roof,
     }
     if flushed is not None:
         # the whole mla_decode_paged call against the path's algorithmic bytes:
         # cache + q in + o_lat out
         t_med = flushed["median_ms"] * 1e-3
-        path_bytes = split_bytes + B * H * wl.d_c * 2
-        flushed.update({"tokens_per_s": round(B / t_med, 1),
+        path_bytes = split_bytes + BQ * H * wl.d_c * 2
+        flushed.update({"tokens_per_s": round(BQ / t_med, 1),
                         "achieved_GBs": round(path_bytes / t_med / 1e9, 1),
                         "achieved_tflops": round(flops / t_med / 1e12, 1),
                         "algorithmic_bytes": path_bytes})
         rec["decode_paged_flushed"] = flushed
     if args.cpu_sample > 0:
-        rec["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample, B))
+        rec["cpu_baseline"] = cpu_baseline(inp, min(max(1, args.cpu_sample // ql), B))
     print(json.dumps(rec), flush=True)
 
 
