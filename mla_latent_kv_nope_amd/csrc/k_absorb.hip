@@ -36,60 +36,19 @@ __device__ __forceinline__ void rope_rotate(float x0, float x1, double s, double
 }
 #pragma clang fp contract(on)
 
-// Workgroups [0, n_gemm): the W_UK GEMM, one head x 128 latent columns
-// (4 waves x 32 columns) x 32 batch rows each; every global load of a wave is
-// in flight at once.  Workgroups [n_gemm, n_gemm + B * ceil(H / 32)): the RoPE
-// half of the query for one batch row and 32 heads; the d_rope/2 angles of the
-// row's position are evaluated once per workgroup.
+// One workgroup per (head h, 128 latent columns, 32 batch rows): the W_UK
+// GEMM of that tile (4 waves x 32 columns), plus the RoPE half of the query for
+// its share of the rows: the NCB column-block workgroups of a (head, 32 rows)
+// tile each rotate 32 / NCB rows, one (row, pair) per thread with its angle
+// evaluated in fp64.  Every workgroup needs 40 KB of LDS, so four fit on a CU
+// and a 64-row batch at 128 heads runs in a single round of 1024 workgroups.
 template <int DC, int DN>
-__global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a, int n_gemm) {
+__global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
   constexpr int COLS = DC < 128 ? DC : 128;  // latent columns per workgroup
   constexpr int NCB = DC / COLS;             // column blocks per head
-  static_assert(COLS % 32 == 0 && DN % 16 == 0, "tile shape");
+  static_assert(COLS % 32 == 0 && DN % 16 == 0 && 32 % NCB == 0, "tile shape");
   const int B = a.B, H = a.H;
   const int R = DC + a.d_rope;
-
-  if (static_cast<int>(blockIdx.x) >= n_gemm) {
-    // RoPE workgroup: batch row b, heads [hb, hb + 32); one pair per thread and
-    // pass, all loads of the workgroup in flight together
-    constexpr int HPW = 32;                    // heads per RoPE workgroup
-    __shared__ double sc[2][64];
-    const int id = blockIdx.x - n_gemm;
-    const int hgrp = (H + HPW - 1) / HPW;
-    const int b = id / hgrp, hb = (id - b * hgrp) * HPW;
-    const int pairs = a.d_rope / 2;            // <= 32
-    if (static_cast<int>(threadIdx.x) < pairs) {
-      double sn, cs;
-      rope_angle(threadIdx.x, a.d_rope, a.q_pos[b], a.rope_base, &sn, &cs);
-      sc[0][threadIdx.x] = sn;
-      sc[1][threadIdx.x] = cs;
-    }
-    constexpr int PASSES = HPW * 32 / 256;
-    uint32_t v[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int idx = p * 256 + threadIdx.x;
-      const int h = hb + idx / pairs, i = idx % pairs;
-      v[p] = (idx < HPW * pairs && h < H)
-                 ? *reinterpret_cast<const uint32_t*>(a.q_pe + (static_cast<int64_t>(b) * H + h) * a.d_rope + 2 * i)
-                 : 0u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int idx = p * 256 + threadIdx.x;
-      const int h = hb + idx / pairs, i = idx % pairs;
-      if (idx < HPW * pairs && h < H) {
-        float y0, y1;
-        rope_rotate(bf16_bits_to_f32(static_cast<uint16_t>(v[p] & 0xffffu)),
-                    bf16_bits_to_f32(static_cast<uint16_t>(v[p] >> 16)), sc[0][i], sc[1][i], &y0, &y1);
-        const uint32_t packed = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
-                                (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
-        *reinterpret_cast<uint32_t*>(a.q_out + (static_cast<int64_t>(b) * H + h) * R + DC + 2 * i) = packed;
-      }
-    }
-    return;
-  }
 
   // GEMM workgroup: head h, latent columns [cbk*COLS, +COLS), batch rows
   // [b0, b0 + 32).  The W_UK slice and the q_nope rows are copied into LDS with
@@ -100,9 +59,13 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a, int n_gemm) {
   constexpr int ROWB = DN * 2;
   static_assert((CH & (CH - 1)) == 0 && (COLS * ROWB) % 1024 == 0 && (32 * ROWB) % 1024 == 0,
                 "copy shapes");
-  __shared__ __attribute__((aligned(1024))) char wl[COLS * ROWB];   // W_UK slice [COLS][DN]
+  // the W_UK slice [COLS][DN]; after the MFMAs, the result [32][COLS] (padded
+  // rows) in the same space
+  constexpr int WL_BYTES = COLS * ROWB;
+  constexpr int OL_BYTES = 32 * (COLS + 8) * 2;
+  __shared__ __attribute__((aligned(1024))) char wl[WL_BYTES > OL_BYTES ? WL_BYTES : OL_BYTES];
   __shared__ __attribute__((aligned(1024))) char ql[32 * ROWB];     // q_nope rows [32][DN]
-  __shared__ __attribute__((aligned(16))) uint16_t ol[32 * (COLS + 8)];  // result [32][COLS]
+  uint16_t* const ol = reinterpret_cast<uint16_t*>(wl);
   int id = blockIdx.x;
   const int cbk = id % NCB;
   id /= NCB;
@@ -110,6 +73,17 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a, int n_gemm) {
   const int b0 = (id / H) * 32;              // batch rows [b0, b0 + 32)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int NWAVES = 4;
+
+  // RoPE half of the query: rows [b0 + cbk * RPW, +RPW) of head h, one
+  // (row, pair) per thread; its q_pe load is issued with the copies below
+  constexpr int RPW = 32 / NCB;              // rows rotated by this workgroup
+  const int pairs = a.d_rope / 2;
+  const int rrow = static_cast<int>(threadIdx.x) / pairs, rpair = static_cast<int>(threadIdx.x) - rrow * pairs;
+  const int rb = b0 + cbk * RPW + rrow;
+  const bool rope_lane = rrow < RPW && rb < B;
+  const uint32_t qpe =
+      rope_lane ? *reinterpret_cast<const uint32_t*>(a.q_pe + (static_cast<int64_t>(rb) * H + h) * a.d_rope + 2 * rpair)
+                : 0u;
 
   // copies: lane l of 1 KB block k fills row (1024k + 16l) / ROWB, chunk
   // position p = l % CH with source chunk p ^ (row % CH)
@@ -125,15 +99,37 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a, int n_gemm) {
     const uint16_t* src = a.q_nope + (static_cast<int64_t>(br) * H + h) * DN + 8 * (pch ^ (r % CH));
     lds_dma16_v(src, lds_addr(ql + 1024 * k));
   }
+  // the angle needs only the row's position: read with scalar loads (their
+  // own counter), it is evaluated while the copies are in flight
+  // (q_pos is read-only for the whole kernel; the constant address space
+  // lets the compiler use scalar loads)
+  const auto* qpos_c = (const __attribute__((address_space(4))) int32_t*)(a.q_pos);
+  int rpos = 0;
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int bj = b0 + cbk * RPW + j;
+    const int pj = bj < B ? qpos_c[bj] : 0;
+    rpos = rrow == j ? pj : rpos;
+  }
+  double sn = 0.0, cs = 1.0;
+  if (rope_lane) rope_angle(rpair, a.d_rope, rpos, a.rope_base, &sn, &cs);
   wait_vmcnt<0>();
+  if (rope_lane) {
+    float y0, y1;
+    rope_rotate(bf16_bits_to_f32(static_cast<uint16_t>(qpe & 0xffffu)),
+                bf16_bits_to_f32(static_cast<uint16_t>(qpe >> 16)), sn, cs, &y0, &y1);
+    const uint32_t packed = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
+                            (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+    *reinterpret_cast<uint32_t*>(a.q_out + (static_cast<int64_t>(rb) * H + h) * R + DC + 2 * rpair) = packed;
+  }
   __syncthreads();
 
+  f32x16 acc = {};
+  const int r = lane & 31, half = lane >> 5;
+  const int cw = wave * 32 + r;
   if (wave < COLS / 32) {
     // A = q rows (lane: row l%32, k = 8(l/32) + [0,8) of each 16-wide step),
     // B = W_UK rows (lane: column l%32, same k)
-    const int r = lane & 31, half = lane >> 5;
-    const int cw = wave * 32 + r;
-    f32x16 acc = {};
 #pragma unroll
     for (int k = 0; k < DN / 16; ++k) {
       const int ch = 2 * k + half;
@@ -141,6 +137,9 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a, int n_gemm) {
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(wl + cw * ROWB + 16 * (ch ^ (cw % CH)));
       acc = mfma32(av, bv, acc);
     }
+  }
+  __syncthreads();                           // the W_UK slice is read; its space takes the result
+  if (wave < COLS / 32) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int rr = 8 * (i >> 2) + 4 * half + (i & 3);
@@ -167,12 +166,11 @@ bool absorb_supported(int d_c, int d_nope) {
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s) {
   const dim3 block(256);
   const int rb = (a.B + 31) / 32;
+  if (a.d_rope / 2 * (32 / (a.d_c < 128 ? 1 : a.d_c / 128)) > 256) return hipErrorInvalidValue;
   if (a.d_c == 512 && a.d_nope == 128) {
-    const int n_gemm = a.H * 4 * rb;
-    hipLaunchKernelGGL((k_absorb<512, 128>), dim3(n_gemm + a.B * ((a.H + 31) / 32)), block, 0, s, a, n_gemm);
+    hipLaunchKernelGGL((k_absorb<512, 128>), dim3(a.H * 4 * rb), block, 0, s, a);
   } else if (a.d_c == 32 && a.d_nope == 16) {
-    const int n_gemm = a.H * rb;
-    hipLaunchKernelGGL((k_absorb<32, 16>), dim3(n_gemm + a.B * ((a.H + 31) / 32)), block, 0, s, a, n_gemm);
+    hipLaunchKernelGGL((k_absorb<32, 16>), dim3(a.H * rb), block, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
