@@ -27,6 +27,33 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to the even significand),
+    for finite values whose result is finite.  The candidates are the bf16
+    values just below and above x (truncations of x's binary32 neighbours);
+    the decision is made on the exact float64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)                       # nearest binary32 (for the neighbours only)
+    u = f.view(np.uint32)
+    lo = (u & np.uint32(0xFFFF0000))               # truncation toward zero in magnitude
+    lo_v = lo.view(np.float32).astype(np.float64)
+    # the other candidate is one bf16 step further from zero
+    hi = (lo + np.uint32(0x10000)).astype(np.uint32)
+    hi_v = hi.view(np.float32).astype(np.float64)
+    # make (a, b) the candidates bracketing x
+    below = np.abs(lo_v) <= np.abs(x)
+    a_bits = np.where(below, lo, (lo - np.uint32(0x10000)).astype(np.uint32))
+    b_bits = np.where(below, hi, lo)
+    a_v = a_bits.view(np.float32).astype(np.float64)
+    b_v = b_bits.view(np.float32).astype(np.float64)
+    da, db = np.abs(x - a_v), np.abs(b_v - x)
+    even_a = ((a_bits >> np.uint32(16)) & np.uint32(1)) == 0
+    pick_a = (da < db) | ((da == db) & even_a)
+    out = np.where(pick_a, a_bits, b_bits) >> np.uint32(16)
+    out = np.where(x == 0, (u >> np.uint32(16)), out)   # +-0 keep their sign
+    return out.astype(np.uint16)
+
+
 def e4m3fn_decode(codes: np.ndarray) -> np.ndarray:
     """Value of each E4M3FN code (uint8) as float64; NaN codes give NaN."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)

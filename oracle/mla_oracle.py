@@ -38,7 +38,7 @@ import math
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode_satfinite, E4M3_MAX
+from .codecs import bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode_satfinite, f64_to_bf16_bits, E4M3_MAX
 
 
 # ----------------------------------------------------------------------------
@@ -57,6 +57,26 @@ def mla_cache_bytes_per_token(d_c: int, d_rope: int, fp8: bool) -> int:
     """One layer: bf16 rows are 2 bytes per element; fp8 rows are 1 byte per
     element plus one fp32 scale."""
     return (d_c + d_rope) + 4 if fp8 else 2 * (d_c + d_rope)
+
+
+# ----------------------------------------------------------------------------
+# Down-projection of the hidden state into the cached latent
+# ----------------------------------------------------------------------------
+def project_latent(h_bits: np.ndarray, w_down_bits: np.ndarray, d_c: int):
+    """c_kv and the un-rotated key RoPE part of new tokens from their hidden
+    states: the latent is the down-projection of h ("DeepSeek-V2拆解" §2.1:
+    `down_proj = nn.Linear(d_model, kv_rank)`, c_kv = down_proj(h), then
+    appended to the cache); the RoPE key comes from h through its own
+    projection in the decoupled branch (same section).  Reading: one weight
+    w_down [d_c + d_rope][d_model] in nn.Linear layout (output rows), W_DKV in
+    rows [0, d_c) and W_KR in rows [d_c, d_c + d_rope); y = h . w_down^T
+    exactly, rounded once to bf16.  Returns (c_kv bits [T][d_c], k_pe bits
+    [T][d_rope]) as uint16, ready for `cache_rows`."""
+    h = bf16_bits_to_f64(h_bits)
+    w = bf16_bits_to_f64(w_down_bits)
+    y = h @ w.T
+    bits = f64_to_bf16_bits(y)
+    return bits[:, :d_c], bits[:, d_c:]
 
 
 # ----------------------------------------------------------------------------

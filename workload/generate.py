@@ -160,3 +160,20 @@ def unused_slots(inp: DecodeInputs):
                     slots.append((p, s))
     spare = [p for p in range(inp.num_pages) if p not in owned]
     return spare, slots
+
+
+@dataclass
+class ProjectionInputs:
+    """Hidden states of new tokens and the down-projection weight (nn.Linear
+    layout: rows are the d_c latent outputs, then the d_rope RoPE-key outputs)."""
+    h: np.ndarray             # uint16 bf16 bits [T][d_model]
+    w_down: np.ndarray        # uint16 bf16 bits [d_c + d_rope][d_model]
+
+
+def make_projection_inputs(n_tokens: int, d_model: int, d_latent: int, seed: int = 0) -> ProjectionInputs:
+    """h ~ N(0, 1), w_down ~ N(0, 1/d_model) (so the projected values have unit
+    variance), drawn in that order from numpy PCG64 `default_rng(seed)`."""
+    rng = np.random.default_rng(seed)
+    h = _normal_bf16(rng, (n_tokens, d_model), 1.0)
+    w = _normal_bf16(rng, (d_latent, d_model), 1.0 / math.sqrt(d_model))
+    return ProjectionInputs(h=h, w_down=w)
