@@ -120,6 +120,36 @@ mla_status_t mla_append_latent(const mla_dims_t* dims, const void* c_kv, const v
                                uint32_t flags, void* stream);
 
 /*
+ * mla_project_append - down-project new tokens' hidden states into latent
+ * rows and append them: mla_append_latent of c_kv = bf16(W_DKV . h) and
+ * k_pe = bf16(W_KR . h).
+ * Source: the cached latent is the down-projection of the hidden state, and
+ * only it is appended to the cache (sheratonhq.com section 2.1, the
+ * down_proj = nn.Linear(d_model, kv_rank) sketch); the RoPE key is projected
+ * in its own decoupled branch (same section); d_model = 7168 for DeepSeek-V3
+ * (zskr.cn section 2.1).
+ *
+ *   d_model     hidden width, a positive multiple of 256 (<= 65536)
+ *   h           bf16 [n_tokens][d_model]
+ *   w_down      bf16 [d_c + d_rope][d_model] (nn.Linear layout): rows
+ *               [0, d_c) are W_DKV, rows [d_c, d_c + d_rope) are W_KR
+ *   workspace   device buffer of at least mla_project_append_workspace_size()
+ *               bytes, 256-byte aligned (fp32 partial sums; no initialisation)
+ *   other arguments as for mla_append_latent (RoPE always applied)
+ * Each output is accumulated in fp32 (in 256-element chunks of d_model, the
+ * chunks added in order) and rounded once to bf16; the row is then stored
+ * exactly as mla_append_latent stores it.  Supported when d_c + d_rope is a
+ * multiple of 32 (else MLA_ERR_UNSUPPORTED).  n_tokens == 0 is a no-op.
+ */
+size_t mla_project_append_workspace_size(const mla_dims_t* dims, int32_t d_model, int32_t n_tokens);
+mla_status_t mla_project_append(const mla_dims_t* dims, int32_t d_model, const void* h,
+                                const void* w_down, const int32_t* positions,
+                                const int32_t* seq_ids, const int32_t* block_table,
+                                int32_t num_seqs, int32_t max_pages, int32_t num_pages,
+                                int32_t n_tokens, void* pool, float* scales, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
  * mla_absorb_q - fold W_UK into the query and rotate the RoPE query part.
  * Source: W_UK is absorbed into the query projection (sheratonhq.com section
  * 2.1); the reordered path multiplies Q by the up-projection weight before

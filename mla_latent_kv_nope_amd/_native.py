@@ -45,7 +45,7 @@ MLA_MAX_Q_LEN = 16
 
 EXPORTS = (
     "mla_append_latent", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_paged",
-    "mla_decode_paged_multi",
+    "mla_decode_paged_multi", "mla_project_append", "mla_project_append_workspace_size",
     "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_last_hip_error",
     "mla_profile_begin", "mla_profile_end",
 )
@@ -74,6 +74,11 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged_multi.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P,
                                            ctypes.c_size_t, _P, _P, _P]
     lib.mla_decode_paged_multi.restype = ctypes.c_int
+    lib.mla_project_append_workspace_size.argtypes = [_DP, _I, _I]
+    lib.mla_project_append_workspace_size.restype = ctypes.c_size_t
+    lib.mla_project_append.argtypes = [_DP, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P,
+                                       ctypes.c_size_t, _P]
+    lib.mla_project_append.restype = ctypes.c_int
     lib.mla_out_proj.argtypes = [_DP, _P, _P, _I, _P, _P]
     lib.mla_out_proj.restype = ctypes.c_int
     lib.mla_cache_bytes_per_token.argtypes = [_DP]

@@ -110,6 +110,43 @@ def append_latent(d: Dims, c_kv: torch.Tensor, k_pe: torch.Tensor, positions: to
     _check("mla_append_latent", st)
 
 
+def project_append_workspace_size(d: Dims, d_model: int, n_tokens: int) -> int:
+    return int(lib.mla_project_append_workspace_size(ctypes.byref(d), int(d_model), int(n_tokens)))
+
+
+def project_append(d: Dims, h: torch.Tensor, w_down: torch.Tensor, positions: torch.Tensor,
+                   seq_ids: torch.Tensor, block_table: torch.Tensor, pool: torch.Tensor,
+                   scales: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> None:
+    """mla_project_append: h [T][d_model], w_down [d_c + d_rope][d_model] (bf16)."""
+    T, d_model = h.shape[0], h.shape[1]
+    R = d.d_c + d.d_rope
+    _req(h, "h", torch.bfloat16, (T, d_model))
+    _req(w_down, "w_down", torch.bfloat16, (R, d_model))
+    _req(positions, "positions", torch.int32, (T,))
+    _req(seq_ids, "seq_ids", torch.int32, (T,))
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs][max_pages]")
+    _req(block_table, "block_table", torch.int32)
+    num_pages = pool.shape[0]
+    if _is_fp8(d):
+        _req(pool, "pool", torch.uint8, pool_shape(d, num_pages))
+        if scales is None:
+            raise ValueError("an fp8 cache needs its scales tensor")
+        _req(scales, "scales", torch.float32, (num_pages, d.page_size))
+    else:
+        _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+    if workspace is None:
+        n = project_append_workspace_size(d, d_model, T)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=h.device)
+    _req(workspace, "workspace", torch.uint8)
+    st = lib.mla_project_append(ctypes.byref(d), d_model, _ptr(h), _ptr(w_down), _ptr(positions),
+                                _ptr(seq_ids), _ptr(block_table), block_table.shape[0],
+                                block_table.shape[1], num_pages, T, _ptr(pool), _ptr(scales),
+                                _ptr(workspace), workspace.numel(), _stream())
+    _check("mla_project_append", st)
+
+
 def absorb_q(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_pos: torch.Tensor,
              w_uk: torch.Tensor, q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     B = q_nope.shape[0]

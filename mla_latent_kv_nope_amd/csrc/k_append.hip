@@ -60,7 +60,9 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, int i, int d_rope,
 }
 #pragma clang fp contract(on)
 
-template <bool FP8>
+// PART: the row comes from fp32 partial sums (summed in chunk order, rounded
+// to bf16) instead of bf16 c_kv / k_pe inputs.
+template <bool FP8, bool PART>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   const int lane = threadIdx.x & 63;
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -78,13 +80,42 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 
   // c_kv: 8 elements per lane
   const bool has_c = 8 * lane < d_c;
-  uint4 cv = make_uint4(0, 0, 0, 0);
-  if (has_c) cv = *reinterpret_cast<const uint4*>(a.c_kv + static_cast<int64_t>(tok) * d_c + 8 * lane);
-  // RoPE pair per lane
   const bool has_r = 2 * lane < d_rope;
+  uint4 cv = make_uint4(0, 0, 0, 0);
+  uint32_t kp = 0;
+  if constexpr (PART) {
+    // sum the reduction chunks of this token's row in order, round to bf16
+    const int64_t stride = static_cast<int64_t>(a.n_tokens) * R;
+    const float* prow = a.part + static_cast<int64_t>(tok) * R;
+    float c[8] = {}, k0 = 0.f, k1 = 0.f;
+    for (int p = 0; p < a.n_part; ++p) {
+      const float* src = prow + p * stride;
+      if (has_c) {
+        const float4 lo = *reinterpret_cast<const float4*>(src + 8 * lane);
+        const float4 hi = *reinterpret_cast<const float4*>(src + 8 * lane + 4);
+        c[0] += lo.x; c[1] += lo.y; c[2] += lo.z; c[3] += lo.w;
+        c[4] += hi.x; c[5] += hi.y; c[6] += hi.z; c[7] += hi.w;
+      }
+      if (has_r) {
+        const float2 kk = *reinterpret_cast<const float2*>(src + d_c + 2 * lane);
+        k0 += kk.x;
+        k1 += kk.y;
+      }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<uint32_t>(f32_to_bf16_bits(c[2 * j])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(c[2 * j + 1])) << 16);
+    cv = make_uint4(w[0], w[1], w[2], w[3]);
+    kp = static_cast<uint32_t>(f32_to_bf16_bits(k0)) | (static_cast<uint32_t>(f32_to_bf16_bits(k1)) << 16);
+  } else {
+    if (has_c) cv = *reinterpret_cast<const uint4*>(a.c_kv + static_cast<int64_t>(tok) * d_c + 8 * lane);
+    if (has_r) kp = *reinterpret_cast<const uint32_t*>(a.k_pe + static_cast<int64_t>(tok) * d_rope + 2 * lane);
+  }
+  // RoPE pair per lane
   float r0 = 0.f, r1 = 0.f;
   if (has_r) {
-    const uint32_t kp = *reinterpret_cast<const uint32_t*>(a.k_pe + static_cast<int64_t>(tok) * d_rope + 2 * lane);
     const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(kp & 0xffffu));
     const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(kp >> 16));
     if (a.rope) rope_pair(x0, x1, lane, d_rope, pos, a.rope_base, &r0, &r1);
@@ -138,8 +169,13 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
   const dim3 grid((a.n_tokens + 3) / 4), block(256);
-  if (a.fp8) hipLaunchKernelGGL(k_append<true>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_append<false>, grid, block, 0, s, a);
+  if (a.part != nullptr) {
+    if (a.fp8) hipLaunchKernelGGL((k_append<true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_append<false, true>), grid, block, 0, s, a);
+  } else {
+    if (a.fp8) hipLaunchKernelGGL((k_append<true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_append<false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

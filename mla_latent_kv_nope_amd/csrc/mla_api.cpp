@@ -123,6 +123,73 @@ mla_status_t mla_append_latent(const mla_dims_t* d, const void* c_kv, const void
   return from_hip(mla::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+bool project_supported(const mla_dims_t* d, int32_t d_model) {
+  return (d->d_c + d->d_rope) % 32 == 0 && d_model > 0 && d_model % mla::kDownChunk == 0 &&
+         d_model <= (1 << 16);
+}
+size_t project_ws_bytes(const mla_dims_t* d, int32_t d_model, int32_t n_tokens) {
+  return sizeof(float) * static_cast<size_t>(d_model / mla::kDownChunk) * static_cast<size_t>(n_tokens) *
+         static_cast<size_t>(d->d_c + d->d_rope);
+}
+}  // namespace
+
+size_t mla_project_append_workspace_size(const mla_dims_t* d, int32_t d_model, int32_t n_tokens) {
+  if (check_dims(d) != MLA_OK || n_tokens < 0 || !project_supported(d, d_model)) return 0;
+  return project_ws_bytes(d, d_model, n_tokens);
+}
+
+mla_status_t mla_project_append(const mla_dims_t* d, int32_t d_model, const void* h, const void* w_down,
+                                const int32_t* positions, const int32_t* seq_ids,
+                                const int32_t* block_table, int32_t num_seqs, int32_t max_pages,
+                                int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  const mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0 || num_seqs <= 0 || max_pages <= 0 || num_pages <= 0 || d_model <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!project_supported(d, d_model)) return MLA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return MLA_OK;
+  if (!h || !w_down || !positions || !seq_ids || !block_table || !pool || !workspace)
+    return MLA_ERR_INVALID_ARG;
+  const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
+  if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(h, 16) || !aligned(w_down, 16) || !aligned(pool, 16) || !aligned(positions, 4) ||
+      !aligned(seq_ids, 4) || !aligned(block_table, 4) || !aligned(workspace, 256) ||
+      (fp8 && !aligned(scales, 4)))
+    return MLA_ERR_INVALID_ARG;
+  if (ws_bytes < project_ws_bytes(d, d_model, n_tokens)) return MLA_ERR_WORKSPACE;
+  mla::ProjectArgs p{};
+  p.T = n_tokens;
+  p.N = d->d_c + d->d_rope;
+  p.d_model = d_model;
+  p.h = static_cast<const uint16_t*>(h);
+  p.w_down = static_cast<const uint16_t*>(w_down);
+  p.part = static_cast<float*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_down(p, s);
+  if (e != hipSuccess) return from_hip(e);
+  mla::AppendArgs a{};
+  a.d_c = d->d_c;
+  a.d_rope = d->d_rope;
+  a.page_size_log2 = log2_exact(d->page_size);
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.num_seqs = num_seqs;
+  a.n_tokens = n_tokens;
+  a.fp8 = fp8;
+  a.rope = true;
+  a.rope_base = d->rope_base;
+  a.part = p.part;
+  a.n_part = d_model / mla::kDownChunk;
+  a.positions = positions;
+  a.seq_ids = seq_ids;
+  a.block_table = block_table;
+  a.pool = pool;
+  a.scales = scales;
+  return from_hip(mla::launch_append(a, s));
+}
+
 mla_status_t mla_absorb_q(const mla_dims_t* d, const void* q_nope, const void* q_pe,
                           const int32_t* q_pos, const void* w_uk, int32_t B, void* q_out,
                           void* stream) {

@@ -21,11 +21,26 @@ struct AppendArgs {
   double rope_base;
   const uint16_t* c_kv;
   const uint16_t* k_pe;
+  // Instead of c_kv / k_pe: fp32 partial rows part[n_part][n_tokens][d_c +
+  // d_rope], summed in order and rounded to bf16 (the down-projection's
+  // reduction chunks).  nullptr = read c_kv / k_pe.
+  const float* part;
+  int n_part;
   const int32_t* positions;
   const int32_t* seq_ids;
   const int32_t* block_table;
   void* pool;
   float* scales;
+};
+
+// Split-K down-projection of mla_project_append: part[ks][t][n] =
+// sum over d_model elements [kDownChunk ks, +kDownChunk) of h[t][k] w_down[n][k].
+constexpr int kDownChunk = 256;
+struct ProjectArgs {
+  int T, N, d_model;         // tokens, outputs (d_c + d_rope), reduction length
+  const uint16_t* h;         // bf16 [T][d_model]
+  const uint16_t* w_down;    // bf16 [N][d_model]
+  float* part;               // fp32 [d_model / kDownChunk][T][N]
 };
 
 struct AbsorbArgs {
@@ -82,6 +97,7 @@ WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts);
 int decode_auto_parts(int B, int H);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_down(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t s);
 // plan + split kernel + combine; `ev0`/`ev1` (may be null) are recorded

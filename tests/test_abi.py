@@ -173,3 +173,25 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+def test_project_append_validation():
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    f = lib.mla_project_append
+    T, dm = 8, 7168
+    need = lib.mla_project_append_workspace_size(ctypes.byref(d), dm, T)
+    assert need == 4 * (dm // 256) * T * 576
+    assert lib.mla_project_append_workspace_size(ctypes.byref(d), 7000, T) == 0   # not a multiple of 256
+    t = mla.make_dims(4, 32, 16, 16, 16, 16)                                     # 48-wide rows
+    assert lib.mla_project_append_workspace_size(ctypes.byref(t), 256, T) == 0
+
+    def call(dm=dm, h=P, ws=P, wsb=need, T=T, dims=d):
+        return f(ctypes.byref(dims), dm, h, P, P, P, P, 4, 8, 40, T, P, None, ws, wsb, None)
+
+    _expect(call(dm=7000), _native.MLA_ERR_UNSUPPORTED)
+    _expect(call(dims=t, dm=256), _native.MLA_ERR_UNSUPPORTED)
+    _expect(call(dm=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(wsb=need - 1), _native.MLA_ERR_WORKSPACE)
+    _expect(call(ws=P + 16), _native.MLA_ERR_INVALID_ARG)        # workspace not 256-aligned
+    _expect(call(h=None), _native.MLA_ERR_INVALID_ARG)
+    assert call(T=0) == _native.MLA_OK                           # no tokens: nothing enqueued
