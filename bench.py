@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--flushed-iters", type=int, default=50,
                     help="decode-only iterations, each after reading 768 MiB of other data "
                          "(evicts the Infinity Cache), for the median / p10 / p90 (0 = skip)")
+    ap.add_argument("--op", default="step", choices=["step", "project_append"],
+                    help="step: the decode step (default); project_append: mla_project_append "
+                         "alone for one decode step's new tokens (B=64, d_model=7168, V3 rows)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three device-to-device copies of MIB MiB (a kernel of known "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -92,6 +95,61 @@ def measured_traffic(workload: str):
         except OSError:
             return None
     return int(block["traffic_bytes_per_launch"])
+
+
+def bench_project_append(args):
+    """mla_project_append for the 64 new tokens of a V3 decode step: hidden
+    states [64][7168] projected by w_down [576][7168] and appended at position
+    8191 of 64 sequences (permuted pages).  The roof is HBM: the weight, the
+    hidden states and the rows written, each moved once."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_nope_amd as mla
+    from workload import configs, make_projection_inputs
+    from workload.torch_io import bf16_tensor
+
+    wl, d_model = configs.V3, 7168
+    B, S, R = wl.batch, wl.seq_len, wl.d_latent
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    d = mla.make_dims(wl.n_heads, wl.d_c, wl.d_rope, wl.d_nope, wl.d_v, wl.page_size,
+                      softmax_scale=wl.softmax_scale, rope_base=wl.rope_base)
+    pin = make_projection_inputs(B, d_model, R, seed=0)
+    h, w = bf16_tensor(pin.h, dev), bf16_tensor(pin.w_down, dev)
+    mp = S // wl.page_size
+    rng = np.random.default_rng(0)
+    bt = torch.from_numpy(rng.permutation(B * mp).astype(np.int32).reshape(B, mp)).to(dev)
+    pool, _ = mla.new_pool(d, B * mp, dev)
+    pos = torch.full((B,), S - 1, dtype=torch.int32, device=dev)
+    sid = torch.arange(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(mla.project_append_workspace_size(d, d_model, B), dtype=torch.uint8, device=dev)
+    call = lambda: mla.project_append(d, h, w, pos, sid, bt, pool, None, ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    nbytes = R * d_model * 2 + B * d_model * 2 + B * R * 2
+    flops = 2.0 * B * R * d_model
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "mla_project_append time per decode step (64 new tokens)", "value": round(us, 3),
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "V3 decode step's new tokens: T=64, d_model=7168 -> 576-wide rows, "
+                               "page 64, permuted pages", "tokens": B, "d_model": d_model,
+                   "kernels": "k_down (split-K, 18 x 28 workgroups) + k_append (chunk sum)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_call": nbytes, "flops_per_call": flops,
+                     "note": "both kernels of the call, back to back; HIP events on the stream"},
+    }), flush=True)
 
 
 def cpu_baseline(inp, n_seq: int):
@@ -172,6 +230,9 @@ def main():
               "(attention data parallel) and needs no collective, but multi-GPU runs are not "
               "part of it. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.op == "project_append":
+        bench_project_append(args)
+        return
 
     import numpy as np
     import torch

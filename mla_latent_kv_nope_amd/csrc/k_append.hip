@@ -87,19 +87,28 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     // sum the reduction chunks of this token's row in order, round to bf16
     const int64_t stride = static_cast<int64_t>(a.n_tokens) * R;
     const float* prow = a.part + static_cast<int64_t>(tok) * R;
+    // eight chunks' loads in flight at a time, then added in chunk order
+    constexpr int U = 8;
     float c[8] = {}, k0 = 0.f, k1 = 0.f;
-    for (int p = 0; p < a.n_part; ++p) {
-      const float* src = prow + p * stride;
-      if (has_c) {
-        const float4 lo = *reinterpret_cast<const float4*>(src + 8 * lane);
-        const float4 hi = *reinterpret_cast<const float4*>(src + 8 * lane + 4);
-        c[0] += lo.x; c[1] += lo.y; c[2] += lo.z; c[3] += lo.w;
-        c[4] += hi.x; c[5] += hi.y; c[6] += hi.z; c[7] += hi.w;
+    for (int p0 = 0; p0 < a.n_part; p0 += U) {
+      float4 lo[U], hi[U];
+      float2 kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float* src = prow + static_cast<int64_t>(p0 + u) * stride;
+        const bool live = p0 + u < a.n_part;
+        lo[u] = live && has_c ? *reinterpret_cast<const float4*>(src + 8 * lane) : float4{};
+        hi[u] = live && has_c ? *reinterpret_cast<const float4*>(src + 8 * lane + 4) : float4{};
+        kk[u] = live && has_r ? *reinterpret_cast<const float2*>(src + d_c + 2 * lane) : float2{};
       }
-      if (has_r) {
-        const float2 kk = *reinterpret_cast<const float2*>(src + d_c + 2 * lane);
-        k0 += kk.x;
-        k1 += kk.y;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (p0 + u < a.n_part) {
+          c[0] += lo[u].x; c[1] += lo[u].y; c[2] += lo[u].z; c[3] += lo[u].w;
+          c[4] += hi[u].x; c[5] += hi[u].y; c[6] += hi[u].z; c[7] += hi[u].w;
+          k0 += kk[u].x;
+          k1 += kk[u].y;
+        }
       }
     }
     uint32_t w[4];
