@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--flushed-iters", type=int, default=50,
                     help="decode-only iterations, each after reading 768 MiB of other data "
                          "(evicts the Infinity Cache), for the median / p10 / p90 (0 = skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as a captured HIP graph (replays) instead of eager calls; "
+                         "the eager pass still runs for the split kernel's timing")
     ap.add_argument("--op", default="step", choices=["step", "project_append"],
                     help="step: the decode step (default); project_append: mla_project_append "
                          "alone for one decode step's new tokens (B=64, d_model=7168, V3 rows)")
@@ -307,6 +310,27 @@ def main():
     elapsed = time.perf_counter() - t0
     split_ms_total, n_rec = mla.profile_end()
     assert torch.isfinite(out.float()).all(), "non-finite output"
+    eager_elapsed = elapsed
+    if args.graph:
+        # capture the step (warm-up on the capture stream first), then time replays
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        assert torch.isfinite(out.float()).all(), "non-finite output (graph)"
     flushed = None
     if args.flushed_iters > 0:
         flushed = flushed_decode_times(mla, torch, decode, args.flushed_iters)
@@ -353,8 +377,11 @@ def main():
                             f"append({ql} new tokens per sequence)+absorb+decode_multi(plan,split,"
                             f"combine)+out_proj; value counts the B*q_len new tokens scored")},
         "decode_kernel_tokens_per_s": round(BQ / (split_ms * 1e-3), 1),
+        "launch": "hip graph replay of the captured step" if args.graph else "eager calls",
         "roofline": roof,
     }
+    if args.graph:
+        rec["eager_ms_per_step"] = round(1e3 * eager_elapsed / args.steps, 5)
     if flushed is not None:
         # the whole mla_decode_paged call against the path's algorithmic bytes:
         # cache + q in + o_lat out

@@ -1,0 +1,101 @@
+"""The decode step (append -> absorb -> decode -> out-projection) captured in a
+HIP graph and replayed: the library only enqueues kernels on the caller's
+stream (no allocation, no host synchronisation, no memset), so the step can be
+captured as is.  Every replay, with eager work and synchronisations between
+replays, must give the eager step's outputs bit for bit (the kernels are
+deterministic), also after the inputs are rewritten in place between replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_nope_amd as mla
+from workload import configs, make_inputs
+from workload.torch_io import to_device
+
+from gpu_util import DEV, dims_for, poison_pool
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    configs.V3.with_(name="v3_graph", batch=6, seq_len=None, seq_lens=(1, 40, 700, 64, 2000, 33)),
+    configs.V2LITE.with_(name="v2lite_graph", batch=4, seq_len=None, seq_lens=(100, 1, 900, 64)),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_captured_step_replays_bit_for_bit(wl):
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    t = to_device(inp, DEV)
+    B, H, R = wl.batch, wl.n_heads, wl.d_latent
+    pool, scales = mla.new_pool(d, inp.num_pages, DEV)
+    poison_pool(pool, scales)
+    # the cache holds every token but the last of each sequence; the step
+    # appends the last one
+    last = (inp.cu_seqlens[1:] - 1).astype(np.int64)
+    keep = np.ones(inp.total_tokens, bool)
+    keep[last] = False
+    ik, il = torch.from_numpy(np.nonzero(keep)[0]).to(DEV), torch.from_numpy(last).to(DEV)
+    mla.append_latent(d, t["c_kv"][ik].contiguous(), t["k_pe"][ik].contiguous(),
+                      t["positions"][ik].contiguous(), t["seq_ids"][ik].contiguous(),
+                      t["block_table"], pool, scales)
+    new = {k: t[k][il].contiguous() for k in ("c_kv", "k_pe", "positions", "seq_ids")}
+    ws = mla.new_workspace(d, B, 0, DEV)
+    q = torch.empty((B, H, R), dtype=torch.bfloat16, device=DEV)
+    o_lat = torch.empty((B, H, wl.d_c), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, H, wl.d_v), dtype=torch.bfloat16, device=DEV)
+    q_nope = t["q_nope"].clone()
+
+    def step():
+        mla.append_latent(d, new["c_kv"], new["k_pe"], new["positions"], new["seq_ids"],
+                          t["block_table"], pool, scales)
+        mla.absorb_q(d, q_nope, t["q_pe"], t["q_pos"], t["w_uk"], q)
+        mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], 0, ws, o_lat, lse)
+        mla.out_proj(d, o_lat, t["w_uv"], out)
+
+    def snapshot():
+        return [x.clone() for x in (q, o_lat, lse, out)]
+
+    step()
+    torch.cuda.synchronize()
+    eager = snapshot()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    def same(a, b):
+        return all(torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+                   for x, y in zip(a, b))
+
+    for i in range(4):
+        for x in (q, o_lat, lse, out):           # eager work between replays
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(snapshot(), eager), f"replay {i} differs from the eager step"
+
+    # new query values written in place: the replay reads them
+    q_nope.copy_(torch.flip(t["q_nope"], dims=[0]))
+    step()
+    torch.cuda.synchronize()
+    eager2 = snapshot()
+    assert not same(eager2, eager)
+    for i in range(2):
+        for x in (q, o_lat, lse, out):
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(snapshot(), eager2), f"replay {i} after the input update differs"
