@@ -1330,16 +1330,17 @@ WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = hipSuccess;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+  // d_c 512: eight waves whatever H (<= 128).  With fewer heads the rows past H
+  // carry zero queries and are never stored; the tile stream, not the MFMA
+  // work, sets the time at small H, and one or two waves per workgroup could
+  // not keep enough copies in flight (V2-Lite, H = 16: 145 us with one wave,
+  // against a 9.5 us roofline).
   if (a.d_c == 512 && a.d_rope == 64 && a.fp8) {
-    if (a.H <= 16) e = launch_split<512, 64, 1, true>(a, s);
-    else if (a.H <= 32) e = launch_split<512, 64, 2, true>(a, s);
-    else e = launch_split<512, 64, 8, true>(a, s);
+    e = launch_split<512, 64, 8, true>(a, s);
   } else if (a.fp8) {
     return hipErrorInvalidValue;
   } else if (a.d_c == 512 && a.d_rope == 64) {
-    if (a.H <= 16) e = launch_split<512, 64, 1>(a, s);
-    else if (a.H <= 32) e = launch_split<512, 64, 2>(a, s);
-    else e = launch_split<512, 64, 8>(a, s);
+    e = launch_split<512, 64, 8>(a, s);
   } else if (a.d_c == 32 && a.d_rope == 16) {
     if (a.H <= 16) e = launch_split<32, 16, 1>(a, s);
     else e = launch_split<32, 16, 2>(a, s);

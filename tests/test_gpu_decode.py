@@ -27,6 +27,9 @@ SMALL = [
                          page_size=16),
     configs.V3.with_(name="v3_small", batch=5, seq_len=None, seq_lens=(1, 31, 32, 33, 1500)),
     configs.V3.with_(name="v3_h40", batch=3, n_heads=40, seq_len=None, seq_lens=(64, 77, 1)),
+    # a few heads on the eight-wave kernel: rows past H carry zero queries
+    configs.V3.with_(name="v3_h1", batch=3, n_heads=1, seq_len=None, seq_lens=(5, 100, 33)),
+    configs.V3.with_(name="v3_h3", batch=2, n_heads=3, seq_len=None, seq_lens=(700, 2)),
 ]
 
 
@@ -37,6 +40,7 @@ FP8_SMALL = [
     configs.V3.with_(name="v3_fp8_p16", fp8=True, batch=4, seq_len=None, seq_lens=(17, 100, 5, 700),
                      page_size=16),
     configs.V3.with_(name="v3_fp8_h40", fp8=True, batch=3, n_heads=40, seq_len=None, seq_lens=(64, 77, 1)),
+    configs.V3.with_(name="v3_fp8_h1", fp8=True, batch=2, n_heads=1, seq_len=None, seq_lens=(300, 9)),
     configs.V2LITE.with_(name="v2lite_fp8", fp8=True, batch=3, seq_len=None, seq_lens=(300, 1, 2000)),
     configs.V2LITE.with_(name="v2lite_fp8_h32", fp8=True, batch=2, n_heads=32, seq_len=None,
                          seq_lens=(129, 1000)),
