@@ -626,20 +626,31 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         }
       }
       if (whole) {
-        const auto rs = make_rsrc(a.o_lat + static_cast<int64_t>(b) * H * DC, H * DC * 2);
+        // the tile ring is free: the block goes to LDS as bf16 rows of one
+        // head, then every thread copies whole rows to o_lat with 16-byte
+        // stores.  Rows are 1040 bytes apart, so the rows of a store's four
+        // 16-lane groups (4 rows apart) start 64 bytes apart modulo the 256
+        // bytes of one pass over the banks.
+        constexpr int ROWE = DC + 8;                           // elements per staged row
+        static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::TILE_BYTES, "o_lat staging fits the ring");
+        uint16_t* const st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
         for (int hb = 0; hb < NW; ++hb) {
           if (hb < HB) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int h = hb * 16 + 4 * fq + i;
-              const uint32_t vo = h < H ? static_cast<uint32_t>(h * DC + 16 * cbf + f16) * 2 : 0x80000000u;
 #pragma unroll
               for (int c = 0; c < NC; ++c)
-                __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(oo[hb][c][i])), rs,
-                                                      vo, 32 * c, 0);
+                st[h * ROWE + 16 * (cbf + c) + f16] = f32_to_bf16_bits(oo[hb][c][i]);
             }
           }
+        }
+        __syncthreads();
+        uint4* const dst = reinterpret_cast<uint4*>(a.o_lat + static_cast<int64_t>(b) * H * DC);
+        for (int i = threadIdx.x; i < H * (DC / 8); i += Cfg::THREADS) {
+          const int h = i / (DC / 8), c8 = i - h * (DC / 8);
+          dst[i] = *reinterpret_cast<const uint4*>(st + h * ROWE + 8 * c8);
         }
       } else {
         constexpr uint32_t kBlk = 64 * 8;                      // one 16 x 16 block, bf16
