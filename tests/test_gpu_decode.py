@@ -209,6 +209,17 @@ def test_v3_full_size_sampled():
 
 
 @pytest.mark.slow
+def test_v2lite_full_size_sampled():
+    wl = configs.V2LITE
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    print("[decode v2lite full] B=16 H=16 S=4096", flush=True)
+    res = decode_step(inp, d)
+    assert np.all(np.isfinite(res["out"]))
+    _compare(inp, res, batches=[0, 5, 10, 15])
+
+
+@pytest.mark.slow
 def test_ragged_full_size_sampled():
     wl = configs.RAGGED
     inp = make_inputs(wl)
