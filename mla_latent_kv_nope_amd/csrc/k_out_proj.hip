@@ -93,6 +93,74 @@ __global__ __launch_bounds__(64) void k_out_proj(OutProjArgs a) {
   }
 }
 
+// d_c 512, d_v 128: one workgroup of four waves per (head h, 64 output
+// columns, 64 batch rows); wave w computes the 32 x 32 tile (rows 32 (w & 1),
+// columns 32 (w >> 1)).  The W_UV slice [512][64] (128-byte rows, whole cache
+// lines) and the 64 o_lat rows (1 KB each) are copied global->LDS, so each
+// byte leaves L2 once per workgroup (half the traffic of one wave per 32 x 32
+// tile, which re-read o_lat rows for every column tile).  LDS layouts (16-byte
+// chunks permuted within a row, so every copy still reads whole lines):
+//   W slice: chunk c of row k at c ^ 2 (k mod 4), so the 4 rows x 32 bytes a
+//            transpose read's 16-lane group touches fall in distinct banks;
+//   o_lat:   chunk j of row r at j ^ (r mod 32), so the 32 rows an A-operand
+//            read touches at one column spread over the banks.
+__global__ __launch_bounds__(256) void k_out_proj_w(OutProjArgs a) {
+  constexpr int DC = 512, DV = 128, NC = 64, MR = 64;     // columns, rows per workgroup
+  constexpr int WROW = NC * 2;                            // bytes per W slice row
+  __shared__ __attribute__((aligned(1024))) char wl[DC * WROW];   // 64 KB
+  __shared__ __attribute__((aligned(1024))) char ol[MR * DC * 2]; // 64 KB
+  const int h = blockIdx.x;
+  const int n0 = blockIdx.y * NC;
+  const int b0 = blockIdx.z * MR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int B = a.B, H = a.H;
+
+  // W slice: copy k covers rows 8k .. 8k + 7; lane l fills row 8k + l/8 at
+  // chunk position l % 8 with logical chunk (l % 8) ^ 2 (row mod 4)
+  const uint16_t* wsrc = a.w_uv + static_cast<int64_t>(h) * DC * DV + n0;
+  for (int k = wave; k < DC / 8; k += 4) {
+    const int r = 8 * k + (lane >> 3);
+    const int c = (lane & 7) ^ (2 * (r & 3));
+    lds_dma16_v(wsrc + r * DV + 8 * c, lds_addr(wl + 1024 * k));
+  }
+  // o_lat rows: copy r is row b0 + r; lane l fills chunk position l with
+  // logical chunk l ^ (r mod 32); rows past the batch copy row b0
+  for (int r = wave; r < MR; r += 4) {
+    const int br = b0 + r < B ? b0 + r : b0;
+    const int c = lane ^ (r & 31);
+    lds_dma16_v(a.o_lat + (static_cast<int64_t>(br) * H + h) * DC + 8 * c, lds_addr(ol + 1024 * r));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const int rt = wave & 1, ct = wave >> 1;
+  // A: row 32 rt + l%32, k = 16 s + 8 (l/32) + [0, 8): logical chunk 2 s + l/32
+  const int ar = 32 * rt + (lane & 31), ah = lane >> 5;
+  const char* arow = ol + ar * (DC * 2);
+  // B (transpose reads): source lane 4 rr + q of 16-lane group G reads row
+  // 16 s + 8 (l/32) + rr (+4 for the upper half), columns col0 .. col0 + 3
+  const int G = lane >> 4, j = lane & 15, rr = j >> 2, q = j & 3, g = lane >> 5;
+  const int col0 = 32 * ct + 16 * (G & 1) + 4 * q;       // column within the slice
+  f32x16 acc = {};
+#pragma unroll 8
+  for (int s = 0; s < DC / 16; ++s) {
+    const bf16x8 av = *reinterpret_cast<const bf16x8*>(arow + 16 * ((2 * s + ah) ^ (ar & 31)));
+    const int row = 16 * s + 8 * g + rr;                   // row % 4 == rr
+    const int cb = ((col0 >> 3) ^ (2 * rr)) * 16 + (col0 & 7) * 2;   // byte offset in the row
+    const bf16x4 lo = lds_read_tr16(wl + row * WROW + cb);
+    const bf16x4 hi = lds_read_tr16(wl + (row + 4) * WROW + cb);
+    const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = mfma32(av, bv, acc);
+  }
+  // acc[i]: row 32 rt + 8 (i/4) + 4 (l/32) + i%4, column 32 ct + l%32
+  const int c = n0 + 32 * ct + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int b = b0 + 32 * rt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    if (b < B) a.out[(static_cast<int64_t>(b) * H + h) * DV + c] = f32_to_bf16_bits(acc[i]);
+  }
+}
+
 }  // namespace
 
 bool out_proj_supported(int d_c, int d_v) {
@@ -101,7 +169,7 @@ bool out_proj_supported(int d_c, int d_v) {
 
 hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t s) {
   if (a.d_c == 512 && a.d_v == 128) {
-    hipLaunchKernelGGL((k_out_proj<512, 128>), dim3(a.H, 128 / 32, (a.B + 31) / 32), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_out_proj_w, dim3(a.H, 128 / 64, (a.B + 63) / 64), dim3(256), 0, s, a);
   } else if (a.d_c == 32 && a.d_v == 16) {
     hipLaunchKernelGGL((k_out_proj<32, 16>), dim3(a.H, 1, (a.B + 31) / 32), dim3(64), 0, s, a);
   } else {
