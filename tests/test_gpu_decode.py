@@ -27,6 +27,11 @@ SMALL = [
                          page_size=16),
     configs.V3.with_(name="v3_small", batch=5, seq_len=None, seq_lens=(1, 31, 32, 33, 1500)),
     configs.V3.with_(name="v3_h40", batch=3, n_heads=40, seq_len=None, seq_lens=(64, 77, 1)),
+    # the other supported page sizes (powers of two in [16, 256])
+    configs.V3.with_(name="v3_p32", batch=3, seq_len=None, seq_lens=(31, 100, 700), page_size=32),
+    configs.V3.with_(name="v3_p128", batch=3, seq_len=None, seq_lens=(129, 5, 1000), page_size=128),
+    configs.V3.with_(name="v3_p256", batch=3, seq_len=None, seq_lens=(255, 257, 1500), page_size=256),
+    configs.TINY.with_(name="tiny_p32", page_size=32),
     # a few heads on the eight-wave kernel: rows past H carry zero queries
     configs.V3.with_(name="v3_h1", batch=3, n_heads=1, seq_len=None, seq_lens=(5, 100, 33)),
     configs.V3.with_(name="v3_h3", batch=2, n_heads=3, seq_len=None, seq_lens=(700, 2)),
@@ -41,6 +46,8 @@ FP8_SMALL = [
                      page_size=16),
     configs.V3.with_(name="v3_fp8_h40", fp8=True, batch=3, n_heads=40, seq_len=None, seq_lens=(64, 77, 1)),
     configs.V3.with_(name="v3_fp8_h1", fp8=True, batch=2, n_heads=1, seq_len=None, seq_lens=(300, 9)),
+    configs.V3.with_(name="v3_fp8_p256", fp8=True, batch=2, seq_len=None, seq_lens=(300, 700), page_size=256),
+    configs.V3.with_(name="v3_fp8_p32", fp8=True, batch=2, seq_len=None, seq_lens=(33, 64), page_size=32),
     configs.V2LITE.with_(name="v2lite_fp8", fp8=True, batch=3, seq_len=None, seq_lens=(300, 1, 2000)),
     configs.V2LITE.with_(name="v2lite_fp8_h32", fp8=True, batch=2, n_heads=32, seq_len=None,
                          seq_lens=(129, 1000)),

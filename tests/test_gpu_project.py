@@ -33,6 +33,7 @@ CASES = [
     (configs.V3.with_(name="v3_t70_p16", batch=3, seq_len=None, seq_lens=(33, 2, 35), page_size=16), 768),
     (configs.V2LITE.with_(name="v2_t5", batch=2, seq_len=None, seq_lens=(2, 3)), 2048),
     (configs.V3.with_(name="v3_fp8_t64", batch=2, seq_len=None, seq_lens=(40, 24), fp8=True), 7168),
+    (configs.V3.with_(name="v3_t20_p256", batch=2, seq_len=None, seq_lens=(12, 8), page_size=256), 512),
 ]
 
 
