@@ -8,6 +8,7 @@ from .codecs import bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode_satfinite, f6
 from .mla_oracle import (  # noqa: F401
     absorb_query, cache_rows, fp8_cache_codes, decode_absorbed, decode_explicit, fp8_quantize_rows,
     latent_attention, mha_cache_elements_per_token, mla_cache_bytes_per_token,
-    mla_cache_elements_per_token, out_projection, project_latent, reference_decode, reference_decode_multi, rope,
+    mla_cache_elements_per_token, out_projection, prefill_explicit, project_latent, reference_decode,
+    reference_decode_multi, reference_prefill, rope,
     sequence_rows, softmax_with_lse,
 )

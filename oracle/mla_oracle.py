@@ -305,3 +305,73 @@ def reference_decode_multi(inp, batches=None, heads=None):
                                        wl.softmax_scale, wl.rope_base, heads)
             out[n, i], lse[n, i], o_lat[n, i] = o, l, ol
     return {"out": out, "lse": lse, "o_lat": o_lat}
+
+
+# ----------------------------------------------------------------------------
+# Prefill in the explicit form
+# ----------------------------------------------------------------------------
+def prefill_explicit(q_nope: np.ndarray, q_pe: np.ndarray, C: np.ndarray, Kr: np.ndarray,
+                     w_uk: np.ndarray, w_uv: np.ndarray, q_pos: np.ndarray, scale: float,
+                     base: float, heads=None):
+    """Causal attention of n new tokens of one sequence in the un-absorbed form.
+
+    Reordering by associativity pays off in decode; in prefill it lowers the
+    arithmetic intensity (zskr.cn "LLM推理优化的新范式：从内存墙到计算墙的跨越"
+    §2.2, the per-stage table), so prefill keeps the explicit form: K_h = C @
+    W_UK[h] and V_h = C @ W_UV[h] are materialised from the cached latent, and
+    query i (position q_pos[i]) attends to the tokens t <= q_pos[i] with
+    s_t = scale * (q_nope[i][h] . K_h[t] + RoPE(q_pe[i][h], q_pos[i]) . Kr[t]).
+
+    q_nope [n][H][d_nope], q_pe [n][H][d_rope] (float64, un-rotated); C [S][d_c],
+    Kr [S][d_rope] from `cache_rows`; q_pos int [n].  Returns out [n][nh][d_v]
+    and lse [n][nh]; a query with no visible token (q_pos < 0) gives out = 0 and
+    lse = -inf.
+    """
+    n, H = q_nope.shape[0], q_nope.shape[1]
+    heads = list(range(H)) if heads is None else list(heads)
+    d_v = w_uv.shape[2]
+    S = C.shape[0]
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    out = np.zeros((n, len(heads), d_v))
+    lse = np.full((n, len(heads)), -np.inf)
+    if S == 0 or n == 0:
+        return out, lse
+    visible = np.arange(S)[None, :] <= q_pos[:, None]            # [n][S]
+    live = visible.any(axis=1)
+    qr = rope(q_pe[:, heads], q_pos[:, None], base)             # [n][nh][d_rope]
+    for j, h in enumerate(heads):
+        K = C @ w_uk[h]                                           # [S][d_nope]
+        V = C @ w_uv[h]                                           # [S][d_v]
+        s = scale * (q_nope[:, h] @ K.T + qr[:, j] @ Kr.T)        # [n][S]
+        s = np.where(visible, s, -np.inf)
+        p, l = softmax_with_lse(s[live])
+        out[live, j] = p @ V
+        lse[live, j] = l
+    return out, lse
+
+
+def reference_prefill(inp, batches=None, heads=None, rows=None):
+    """`prefill_explicit` over (a subset of) a generated batch whose q_len new
+    tokens per sequence are the last q_len cached ones: new token i of
+    sequence b sits at position S_b - q_len + i (the reading used for the
+    multi-token query, extended to a whole chunk).  `rows` picks new tokens
+    (default: all).  Returns out [nb][nr][nh][d_v] and lse [nb][nr][nh]."""
+    wl = inp.wl
+    ql, H = wl.q_len, wl.n_heads
+    B = len(inp.seq_lens)
+    batches = list(range(B)) if batches is None else list(batches)
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = list(range(ql)) if rows is None else list(rows)
+    w_uk = bf16_bits_to_f64(inp.w_uk)
+    w_uv = bf16_bits_to_f64(inp.w_uv)
+    out = np.zeros((len(batches), len(rows), len(heads), wl.d_v))
+    lse = np.zeros((len(batches), len(rows), len(heads)))
+    for n, b in enumerate(batches):
+        C, Kr = sequence_rows(inp, b)
+        S = int(inp.seq_lens[b])
+        qn = bf16_bits_to_f64(inp.q_nope[b]).reshape(ql, H, wl.d_nope)[rows]
+        qp = bf16_bits_to_f64(inp.q_pe[b]).reshape(ql, H, wl.d_rope)[rows]
+        pos = S - ql + np.asarray(rows, dtype=np.int64)
+        out[n], lse[n] = prefill_explicit(qn, qp, C, Kr, w_uk, w_uv, pos, wl.softmax_scale,
+                                          wl.rope_base, heads)
+    return {"out": out, "lse": lse}
