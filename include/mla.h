@@ -150,6 +150,58 @@ mla_status_t mla_project_append(const mla_dims_t* dims, int32_t d_model, const v
                                 size_t ws_bytes, void* stream);
 
 /*
+ * mla_prefill_workspace_size - bytes of device workspace mla_prefill_paged
+ * needs for B sequences whose block-table rows hold max_pages pages: the
+ * per-head K_nope and V of every addressable token, bf16,
+ * 2 * B * n_heads * 128 * round_up(max_pages * page_size, 32) * 2 bytes.
+ * Returns 0 for unsupported dims, B <= 0 or max_pages <= 0.
+ */
+size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t B, int32_t max_pages);
+
+/*
+ * mla_prefill_paged - causal attention of a chunk of new tokens per sequence,
+ * in the explicit form.
+ * Source: reordering by associativity raises decode's arithmetic intensity
+ * but lowers prefill's (zskr.cn section 2.2, the per-stage table), so prefill
+ * materialises K_h = C . W_UK[h] and V_h = C . W_UV[h] from the cached latent
+ * (sheratonhq.com section 2.1) and runs dense attention; long prompts are
+ * processed in chunks (the vLLM deployment page, chunked prefill).
+ *
+ * The chunk's tokens must already be in the cache (mla_append_latent).  The
+ * n_b = q_start[b + 1] - q_start[b] new tokens of sequence b are its last n_b
+ * cached tokens: new token i sits at position seq_lens[b] - n_b + i and
+ * attends to the cached tokens at positions <= its own (a new token at a
+ * negative position sees nothing: out = 0, lse = -inf).
+ *
+ *   q_nope      bf16 [T][H][d_nope]; rows [q_start[b], q_start[b + 1]) are
+ *               sequence b's new tokens in order
+ *   q_pe        bf16 [T][H][d_rope], un-rotated (rotated here at the token's
+ *               position)
+ *   q_start     int32 [B + 1] (device): non-decreasing row offsets
+ *   max_q_len   host bound on n_b: only the first max_q_len new tokens of a
+ *               longer chunk are computed (the others are neither read nor
+ *               written; positions still follow from n_b)
+ *   pool, block_table, max_pages, num_pages, seq_lens: as for
+ *               mla_decode_paged (bf16 cache only)
+ *   w_uk, w_uv  bf16 [H][d_c][d_nope] and [H][d_c][d_v]
+ *   workspace   >= mla_prefill_workspace_size() bytes, 256-byte aligned
+ *   out         bf16 [T][H][d_v] (written): sum_t p_t V_h[t]
+ *   lse         fp32 [T][H] natural-log normaliser of the scores, or NULL
+ * with s_t = softmax_scale * (q_nope . K_h[t] + RoPE(q_pe) . k_rot[t]).
+ * K and V are rounded to bf16 in the workspace, scores and the softmax are
+ * fp32, P is rounded to bf16 for the P.V product.  Supported for d_c 512,
+ * d_rope 64, d_nope = d_v = 128 and a bf16 cache (else MLA_ERR_UNSUPPORTED).
+ * Rows outside [0, T) are neither read nor written.  T == 0 or
+ * max_q_len == 0 is a no-op.
+ */
+mla_status_t mla_prefill_paged(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
+                               const int32_t* q_start, int32_t T, int32_t max_q_len,
+                               const void* pool, const int32_t* block_table, int32_t max_pages,
+                               int32_t num_pages, const int32_t* seq_lens, int32_t B,
+                               const void* w_uk, const void* w_uv, void* workspace,
+                               size_t ws_bytes, void* out, float* lse, void* stream);
+
+/*
  * mla_absorb_q - fold W_UK into the query and rotate the RoPE query part.
  * Source: W_UK is absorbed into the query projection (sheratonhq.com section
  * 2.1); the reordered path multiplies Q by the up-projection weight before
@@ -270,8 +322,8 @@ const char* mla_last_hip_error(void);
 /*
  * Kernel timing hooks for benchmarks (not part of the method).
  * mla_profile_begin(n) creates n pairs of HIP events; while active, each
- * mla_decode_paged call records one pair around its main attention kernel on
- * its stream.  mla_profile_end() waits for the recorded events, writes the
+ * mla_decode_paged, mla_decode_paged_multi and mla_prefill_paged call records
+ * one pair around its main attention kernel on its stream.  mla_profile_end() waits for the recorded events, writes the
  * summed duration in milliseconds and the number of recorded launches, and
  * releases the events.  Not thread-safe; for single-threaded benchmarks only.
  */

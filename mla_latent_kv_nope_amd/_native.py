@@ -47,7 +47,7 @@ EXPORTS = (
     "mla_append_latent", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_paged",
     "mla_decode_paged_multi", "mla_project_append", "mla_project_append_workspace_size",
     "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_last_hip_error",
-    "mla_profile_begin", "mla_profile_end",
+    "mla_profile_begin", "mla_profile_end", "mla_prefill_workspace_size", "mla_prefill_paged",
 )
 
 _P = ctypes.c_void_p
@@ -79,6 +79,11 @@ def _load() -> ctypes.CDLL:
     lib.mla_project_append.argtypes = [_DP, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P,
                                        ctypes.c_size_t, _P]
     lib.mla_project_append.restype = ctypes.c_int
+    lib.mla_prefill_workspace_size.argtypes = [_DP, _I, _I]
+    lib.mla_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.mla_prefill_paged.argtypes = [_DP, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _P, _P, _P,
+                                      ctypes.c_size_t, _P, _P, _P]
+    lib.mla_prefill_paged.restype = ctypes.c_int
     lib.mla_out_proj.argtypes = [_DP, _P, _P, _I, _P, _P]
     lib.mla_out_proj.restype = ctypes.c_int
     lib.mla_cache_bytes_per_token.argtypes = [_DP]

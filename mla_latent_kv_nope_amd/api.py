@@ -274,3 +274,52 @@ def profile_end() -> Tuple[float, int]:
     n = ctypes.c_int32(0)
     _check("mla_profile_end", lib.mla_profile_end(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def prefill_workspace_size(d: Dims, B: int, max_pages: int) -> int:
+    return int(lib.mla_prefill_workspace_size(ctypes.byref(d), int(B), int(max_pages)))
+
+
+def prefill_paged(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_start: torch.Tensor,
+                  max_q_len: int, pool: torch.Tensor, block_table: torch.Tensor,
+                  seq_lens: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """mla_prefill_paged: q_nope [T][H][d_nope], q_pe [T][H][d_rope], q_start [B+1]
+    (device int32); returns out [T][H][d_v] and lse [T][H] (or None)."""
+    H = d.n_heads
+    if q_nope.dim() != 3:
+        raise ValueError("q_nope must be [T][H][d_nope]")
+    T = q_nope.shape[0]
+    B = seq_lens.shape[0]
+    _req(q_nope, "q_nope", torch.bfloat16, (T, H, d.d_nope))
+    _req(q_pe, "q_pe", torch.bfloat16, (T, H, d.d_rope))
+    _req(q_start, "q_start", torch.int32, (B + 1,))
+    num_pages = pool.shape[0]
+    if _is_fp8(d):
+        raise ValueError("mla_prefill_paged reads a bf16 cache")
+    _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages]")
+    _req(block_table, "block_table", torch.int32)
+    _req(seq_lens, "seq_lens", torch.int32, (B,))
+    _req(w_uk, "w_uk", torch.bfloat16, (H, d.d_c, d.d_nope))
+    _req(w_uv, "w_uv", torch.bfloat16, (H, d.d_c, d.d_v))
+    max_pages = block_table.shape[1]
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_size(d, B, max_pages), dtype=torch.uint8,
+                                device=q_nope.device)
+    _req(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((T, H, d.d_v), dtype=torch.bfloat16, device=q_nope.device)
+    _req(out, "out", torch.bfloat16, (T, H, d.d_v))
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
+    if lse is not None:
+        _req(lse, "lse", torch.float32, (T, H))
+    st = lib.mla_prefill_paged(ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(q_start), T,
+                               int(max_q_len), _ptr(pool), _ptr(block_table), max_pages, num_pages,
+                               _ptr(seq_lens), B, _ptr(w_uk), _ptr(w_uv), _ptr(workspace),
+                               workspace.numel(), _ptr(out), _ptr(lse), _stream())
+    _check("mla_prefill_paged", st)
+    return out, lse

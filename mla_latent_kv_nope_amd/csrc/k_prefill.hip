@@ -1,0 +1,386 @@
+// mla_prefill_paged: causal attention of a chunk of new tokens per sequence in
+// the explicit (un-absorbed) form.
+//
+// Method: folding W_UK into the query pays off only in decode; in prefill the
+// reordering lowers the arithmetic intensity (zskr.cn "LLM推理优化的新范式：从内存
+// 墙到计算墙的跨越", section 2.2, the per-stage table), so prefill up-projects
+// the cached latent to per-head K and V (K_h = C . W_UK[h], V_h = C . W_UV[h];
+// "DeepSeek-V2拆解：MLA与MoE如何把KV缓存压降93.3%", sheratonhq.com, section 2.1)
+// and runs dense attention over them, the RoPE key part shared by all heads.
+// Long prompts arrive in chunks ("vLLM 部署 DeepSeek V3" page, chunked prefill
+// of 2048-4096 tokens); a chunk's new token i of sequence b is the cached
+// token at position seq_lens[b] - n_b + i and attends to positions <= its own.
+//
+// Two kernels:
+//   k_up       one workgroup per (head, 64-column half, 1024 tokens), launched
+//              once for K and once for V:
+//              the [512 x 64] weight slice sits in LDS and is read with the
+//              gfx950 transpose read; the latent rows go from the paged pool
+//              straight into MFMA registers.  K_nope is written [t][h][128],
+//              V transposed [h][128][t] (the MFMA operands are swapped for V,
+//              so both stores are 64-byte runs).
+//   k_prefill  one workgroup of four waves per (sequence, head, 128 new
+//              tokens); each wave owns 32 queries.  Keys stream in 32-token
+//              tiles through a two-slot LDS ring filled by global->LDS copies
+//              one tile ahead.  The score tile is computed transposed,
+//              S^T = K . Q^T (32x32x16 bf16 MFMA, Q in registers), so each
+//              lane holds 16 keys of one query: the online-softmax row max
+//              needs one cross-half exchange, and P^T goes straight from the
+//              accumulators into the B operand of O^T = V^T . P^T, whose
+//              accumulators keep the query on the lane as well.
+//   Workgroups of one (sequence, head) sit on one XCD (blockIdx mod 8), so
+//   their K/V tiles are shared through that XCD's L2; the query tiles that
+//   see the most keys start first.
+#include "mla_common.hpp"
+#include "prefill.hpp"
+
+namespace mla {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Page row holding token t of a block-table row (ids outside the pool read
+// page 0: results are then unspecified but every access stays in bounds).
+__device__ __forceinline__ int64_t pool_row(const int32_t* bt_row, int t, int lg, int num_pages) {
+  int page = bt_row[t >> lg];
+  if (static_cast<unsigned>(page) >= static_cast<unsigned>(num_pages)) page = 0;
+  return (static_cast<int64_t>(page) << lg) + (t & ((1 << lg) - 1));
+}
+
+__device__ __forceinline__ int seq_tokens(const PrefillArgs& a, int b) {
+  const int s = a.seq_lens[b];
+  return s < 0 ? 0 : (s > a.s_cap ? a.s_cap : s);
+}
+
+// ---------------------------------------------------------------------------
+// Up-projection
+// ---------------------------------------------------------------------------
+template <bool IS_V>
+__global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
+  constexpr int WROW = 64 * 2;                                // bytes per slice row
+  __shared__ __attribute__((aligned(1024))) char wl[kPfDc * WROW];   // 64 KB
+  const int h = blockIdx.x >> 1;
+  const int n0 = 64 * (blockIdx.x & 1);
+  const int b = blockIdx.z;
+  const int tb = blockIdx.y * kUpTokens;
+  const int S = seq_tokens(a, b);
+  if (tb >= S) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // weight slice [512][64]: chunk c of row k stored at c ^ 2 (k mod 4), so a
+  // transpose read's 16-lane group touches 4 rows in distinct banks
+  const uint16_t* wsrc = (IS_V ? a.w_uv : a.w_uk) + static_cast<int64_t>(h) * kPfDc * kPfDh + n0;
+  for (int k = wave; k < kPfDc / 8; k += 4) {
+    const int r = 8 * k + (lane >> 3);
+    const int c = (lane & 7) ^ (2 * (r & 3));
+    lds_dma16_v(wsrc + r * kPfDh + 8 * c, lds_addr(wl + 1024 * k));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const int r = lane & 31, half = lane >> 5;
+  const int G = lane >> 4, rr = (lane & 15) >> 2, q = lane & 3;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int tend = tb + kUpTokens < S ? tb + kUpTokens : S;
+  for (int t0 = tb + 32 * wave; t0 < tend; t0 += 128) {
+    // latent row of token t0 + r (rows past the sequence repeat its last
+    // token, so every 32-token block the attention reads holds finite values)
+    const int t = t0 + r < S ? t0 + r : S - 1;
+    const uint16_t* crow = a.pool + pool_row(bt, t, a.page_size_log2, a.num_pages) * kPfRow + 8 * half;
+    f32x16 acc[2] = {};
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+      bf16x8 av[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) av[s] = *reinterpret_cast<const bf16x8*>(crow + 16 * (16 * hp + s));
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int row = 16 * (16 * hp + s) + 8 * half + rr;     // row % 4 == rr
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const int col0 = 32 * ct + 16 * (G & 1) + 4 * q;
+          const int cb = ((col0 >> 3) ^ (2 * rr)) * 16 + (col0 & 7) * 2;
+          const bf16x4 lo = lds_read_tr16(wl + row * WROW + cb);
+          const bf16x4 hi = lds_read_tr16(wl + (row + 4) * WROW + cb);
+          const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          if constexpr (IS_V) acc[ct] = mfma32(bv, av[s], acc[ct]);
+          else acc[ct] = mfma32(av[s], bv, acc[ct]);
+        }
+      }
+    }
+    if constexpr (!IS_V) {
+      // acc[ct][i]: token t0 + 8 (i/4) + 4 half + i%4, column n0 + 32 ct + r
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tok = t0 + 8 * (i >> 2) + 4 * half + (i & 3);
+          a.kn[((static_cast<int64_t>(b) * a.s_pad + tok) * a.H + h) * kPfDh + n0 + 32 * ct + r] =
+              f32_to_bf16_bits(acc[ct][i]);
+        }
+    } else {
+      // acc[ct][i]: column n0 + 32 ct + 8 (i/4) + 4 half + i%4, token t0 + r
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int col = n0 + 32 * ct + 8 * (i >> 2) + 4 * half + (i & 3);
+          a.vt[((static_cast<int64_t>(b) * a.H + h) * kPfDh + col) * a.s_pad + t0 + r] =
+              f32_to_bf16_bits(acc[ct][i]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention
+// ---------------------------------------------------------------------------
+// One ring slot: K_nope [32][128] (chunk c of key row r at c ^ (r mod 16)),
+// K_rope [32][64] (chunk c at c ^ (r mod 8)), V^T [128][32] (chunk c of row j
+// at c ^ ((j / 4) mod 4)).
+constexpr int kSlotKn = 0, kSlotKr = 8192, kSlotVt = 12288, kSlotBytes = 20480;
+
+#pragma clang fp contract(off)
+// RoPE pair (x0, x1) at angle pos * base^(-2i / 64): angle, sine, cosine and
+// the rotation in double precision, rounded once to fp32
+__device__ __forceinline__ void rope_pair64(float x0, float x1, int i, int pos, double base,
+                                            float* y0, float* y1) {
+  const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(kPfDr));
+  double s, c;
+  sincos(static_cast<double>(pos) * theta, &s, &c);
+  const double u = static_cast<double>(x0), v = static_cast<double>(x1);
+  const double p0 = u * c;
+  const double p1 = v * s;
+  const double p2 = u * s;
+  const double p3 = v * c;
+  *y0 = static_cast<float>(p0 - p1);
+  *y1 = static_cast<float>(p2 + p3);
+}
+#pragma clang fp contract(on)
+
+__global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kSlotBytes];   // 40 KB
+  const int QT = a.q_tiles;
+  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  const int u = 8 * (slot / QT) + xcd;                 // (sequence, head) unit
+  if (u >= a.B * a.H) return;
+  const int qt = QT - 1 - slot % QT;
+  const int b = u / a.H, h = u - b * a.H;
+  const int q0 = a.q_start[b];
+  const int n = a.q_start[b + 1] - q0;
+  const int nc = min(n, a.max_q_len);                  // new tokens computed
+  if (kPfQTile * qt >= nc) return;
+  const int S = seq_tokens(a, b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 31, half = lane >> 5;
+
+  // keys the workgroup needs: up to the position of its last new token
+  const int last_i = min(kPfQTile * qt + kPfQTile - 1, nc - 1);
+  const int kend = min(S, S - n + last_i + 1);
+  const int NT = kend > 0 ? (kend + kPfKTile - 1) / kPfKTile : 0;
+  // this wave's queries and their positions (-1: sees nothing)
+  const int i = kPfQTile * qt + 32 * wave + r;
+  const int row = q0 + i;
+  const bool live = i < nc && row >= 0 && row < a.T;
+  const int pos = i < nc ? S - n + i : -1;
+  const int wlast = min(kPfQTile * qt + 32 * wave + 31, nc - 1);
+  const int pw = kPfQTile * qt + 32 * wave < nc ? S - n + wlast : -1;   // wave's last position
+
+  // Q as the B operand: step s < 8 holds q_nope[16 s + 8 half, +8), steps
+  // 8..11 the rotated q_pe[16 (s - 8) + 8 half, +8) (pairs 8 (s - 8) + 4 half + e)
+  bf16x8 qv[12];
+  const bf16x8 zero = {};
+  if (live) {
+    const uint16_t* qn = a.q_nope + (static_cast<int64_t>(row) * a.H + h) * kPfDh + 8 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] = *reinterpret_cast<const bf16x8*>(qn + 16 * s);
+    const uint16_t* qp = a.q_pe + (static_cast<int64_t>(row) * a.H + h) * kPfDr + 8 * half;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * s);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y0, y1;
+        rope_pair64(bf16_bits_to_f32(static_cast<uint16_t>(w[e] & 0xffffu)),
+                    bf16_bits_to_f32(static_cast<uint16_t>(w[e] >> 16)), 8 * s + 4 * half + e, pos,
+                    a.rope_base, &y0, &y1);
+        o[e] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
+               (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+      }
+      qv[8 + s] = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 12; ++s) qv[s] = zero;
+  }
+
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  const uint16_t* kn_b = a.kn + static_cast<int64_t>(b) * a.s_pad * a.H * kPfDh;
+  const uint16_t* vt_bh = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * a.s_pad;
+  // copies of key tile nt into slot base: 8 K_nope, 4 K_rope and 8 V^T copies
+  // of 1 KB, five per wave; lane l of a copy fills LDS bytes [16 l, +16)
+  auto issue = [&](int nt, char* base) {
+    const int t0 = kPfKTile * nt;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int k = wave + 4 * k2;
+      const int kr = 4 * k + (lane >> 4);
+      const int lc = (lane & 15) ^ (kr & 15);
+      lds_dma16_v(kn_b + (static_cast<int64_t>(t0 + kr) * a.H + h) * kPfDh + 8 * lc,
+                  lds_addr(base + kSlotKn + 1024 * k));
+    }
+    {
+      const int kr = 8 * wave + (lane >> 3);
+      const int lc = (lane & 7) ^ (kr & 7);
+      const int t = t0 + kr < S ? t0 + kr : S - 1;
+      lds_dma16_v(a.pool + pool_row(bt, t, a.page_size_log2, a.num_pages) * kPfRow + kPfDc + 8 * lc,
+                  lds_addr(base + kSlotKr + 1024 * wave));
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int k = wave + 4 * k2;
+      const int j = 16 * k + (lane >> 2);
+      const int lc = (lane & 3) ^ ((j >> 2) & 3);
+      lds_dma16_v(vt_bh + static_cast<int64_t>(j) * a.s_pad + t0 + 8 * lc,
+                  lds_addr(base + kSlotVt + 1024 * k));
+    }
+  };
+
+  float m = kNegInf, l = 0.f;
+  f32x16 o[4] = {};
+  if (NT > 0) issue(0, lds);
+  for (int nt = 0; nt < NT; ++nt) {
+    wait_vmcnt<0>();
+    __syncthreads();                       // tile nt landed; slot (nt + 1) % 2 is free
+    if (nt + 1 < NT) issue(nt + 1, lds + ((nt + 1) & 1) * kSlotBytes);
+    const int t0 = kPfKTile * nt;
+    if (t0 > pw) continue;                 // every key of the tile is after this wave's queries
+    const char* sb = lds + (nt & 1) * kSlotBytes;
+
+    // S^T tile: acc[e] is key t0 + 8 (e/4) + 4 half + e%4 of query r
+    f32x16 sacc = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(sb + kSlotKn + r * 256 + 16 * ((2 * s + half) ^ (r & 15)));
+      sacc = mfma32(kv, qv[s], sacc);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(sb + kSlotKr + r * 128 + 16 * ((2 * s + half) ^ (r & 7)));
+      sacc = mfma32(kv, qv[8 + s], sacc);
+    }
+
+    // online softmax in base 2; masked keys are -inf, and a query that has
+    // seen no key yet keeps m = -inf with offset 0 (so p = 0, not NaN)
+    float tmax = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = t0 + 8 * (e >> 2) + 4 * half + (e & 3);
+      const float x = key <= pos ? sacc[e] * a.scale_log2 : kNegInf;
+      sacc[e] = x;
+      tmax = fmaxf(tmax, x);
+    }
+    tmax = max_across_half_waves(tmax);
+    const float mn = fmaxf(m, tmax);
+    const float mu = mn == kNegInf ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mu);
+    m = mn;
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sacc[e] - mu);
+      sacc[e] = p;
+      ls += p;
+    }
+    l = l * alpha + ls;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
+
+    // O^T += V^T . P^T over the 32 keys in two 16-key steps; step s2 uses the
+    // keys {16 s2 + 4 half + [0,4), 16 s2 + 8 + 4 half + [0,4)} on both sides
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint4 pk = make_uint4(pack_bf16x2(sacc[8 * s2 + 0], sacc[8 * s2 + 1]),
+                                  pack_bf16x2(sacc[8 * s2 + 2], sacc[8 * s2 + 3]),
+                                  pack_bf16x2(sacc[8 * s2 + 4], sacc[8 * s2 + 5]),
+                                  pack_bf16x2(sacc[8 * s2 + 6], sacc[8 * s2 + 7]));
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int j = 32 * cb + r;
+        const char* vrow = sb + kSlotVt + j * 64 + 8 * half;
+        const int sw = (j >> 2) & 3;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * ((2 * s2) ^ sw));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * ((2 * s2 + 1) ^ sw));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[cb] = mfma32(va, pb, o[cb]);
+      }
+    }
+  }
+
+  // normalise; o[cb][e] is O[query r][32 cb + 8 (e/4) + 4 half + e%4]
+  const float lt = sum_across_half_waves(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  __syncthreads();                         // every wave is done with the ring
+  char* st = lds + 8192 * wave;            // [32 queries][128] bf16, chunk c at c ^ (query mod 16)
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint2 v = make_uint2(pack_bf16x2(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv),
+                                 pack_bf16x2(o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv));
+      *reinterpret_cast<uint2*>(st + r * 256 + 16 * ((4 * cb + g) ^ (r & 15)) + 8 * half) = v;
+    }
+  if (live && half == 0 && a.lse != nullptr)
+    a.lse[static_cast<int64_t>(row) * a.H + h] =
+        lt > 0.f ? (m + __builtin_log2f(lt)) * 0.69314718055994531f : kNegInf;
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int k = lane + 64 * it;
+    const int qr = k >> 4, c = k & 15;
+    const int qi = kPfQTile * qt + 32 * wave + qr;
+    const int orow = q0 + qi;
+    if (qi < nc && orow >= 0 && orow < a.T) {
+      const uint4 v = *reinterpret_cast<const uint4*>(st + qr * 256 + 16 * (c ^ (qr & 15)));
+      *reinterpret_cast<uint4*>(a.out + (static_cast<int64_t>(orow) * a.H + h) * kPfDh + 8 * c) = v;
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(int d_c, int d_rope, int d_nope, int d_v, bool fp8) {
+  return d_c == kPfDc && d_rope == kPfDr && d_nope == kPfDh && d_v == kPfDh && !fp8;
+}
+
+int64_t prefill_s_pad(int64_t s_cap) { return (s_cap + kPfKTile - 1) / kPfKTile * kPfKTile; }
+
+size_t prefill_workspace_bytes(int B, int H, int64_t s_cap) {
+  const size_t one = static_cast<size_t>(B) * H * kPfDh * prefill_s_pad(s_cap) * 2;
+  const size_t al = (one + 255) / 256 * 256;
+  return 2 * al;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, hipEvent_t up0, hipEvent_t up1,
+                          hipEvent_t at0, hipEvent_t at1) {
+  if (a.B <= 0 || a.T <= 0 || a.q_tiles <= 0) return hipSuccess;
+  const int64_t units = (static_cast<int64_t>(a.B) * a.H + 7) / 8 * 8;
+  const int64_t grid = units * a.q_tiles;
+  if (grid > 0x7fffffff || a.B > 65535) return hipErrorInvalidValue;
+  const int ytiles = (a.s_cap + kUpTokens - 1) / kUpTokens;
+  if (up0) (void)hipEventRecord(up0, s);
+  hipLaunchKernelGGL(k_up<false>, dim3(2 * a.H, ytiles, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_up<true>, dim3(2 * a.H, ytiles, a.B), dim3(256), 0, s, a);
+  if (up1) (void)hipEventRecord(up1, s);
+  if (at0) (void)hipEventRecord(at0, s);
+  hipLaunchKernelGGL(k_prefill, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+  if (at1) (void)hipEventRecord(at1, s);
+  return hipGetLastError();
+}
+
+}  // namespace mla

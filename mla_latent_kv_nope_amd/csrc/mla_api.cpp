@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "mla_internal.hpp"
+#include "prefill.hpp"
 
 namespace {
 
@@ -299,6 +300,77 @@ mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const vo
                                     float* lse, void* stream) {
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
                      num_splits, workspace, ws_bytes, o_lat, lse, stream);
+}
+
+size_t mla_prefill_workspace_size(const mla_dims_t* d, int32_t B, int32_t max_pages) {
+  if (check_dims(d) != MLA_OK || B <= 0 || max_pages <= 0) return 0;
+  if (!mla::prefill_supported(d->d_c, d->d_rope, d->d_nope, d->d_v, d->cache_dtype == MLA_CACHE_FP8_E4M3))
+    return 0;
+  const int64_t s_cap = static_cast<int64_t>(max_pages) * d->page_size;
+  if (s_cap > (int64_t{1} << 24)) return 0;
+  return mla::prefill_workspace_bytes(B, d->n_heads, s_cap);
+}
+
+mla_status_t mla_prefill_paged(const mla_dims_t* d, const void* q_nope, const void* q_pe,
+                               const int32_t* q_start, int32_t T, int32_t max_q_len,
+                               const void* pool, const int32_t* block_table, int32_t max_pages,
+                               int32_t num_pages, const int32_t* seq_lens, int32_t B,
+                               const void* w_uk, const void* w_uv, void* workspace,
+                               size_t ws_bytes, void* out, float* lse, void* stream) {
+  const mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (T < 0 || max_q_len < 0 || B <= 0 || max_pages <= 0 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
+  if (!mla::prefill_supported(d->d_c, d->d_rope, d->d_nope, d->d_v, d->cache_dtype == MLA_CACHE_FP8_E4M3))
+    return MLA_ERR_UNSUPPORTED;
+  const int64_t s_cap = static_cast<int64_t>(max_pages) * d->page_size;
+  if (s_cap > (int64_t{1} << 24)) return MLA_ERR_UNSUPPORTED;
+  if (B > 65535 || max_q_len > (1 << 24) ||
+      (static_cast<int64_t>(B) * d->n_heads + 7) / 8 * 8 * ((max_q_len + mla::kPfQTile - 1) / mla::kPfQTile) >
+          0x7fffffff)
+    return MLA_ERR_UNSUPPORTED;
+  if (T == 0 || max_q_len == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !q_start || !pool || !block_table || !seq_lens || !w_uk || !w_uv ||
+      !workspace || !out)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(q_start, 4) || !aligned(pool, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
+      !aligned(workspace, 256) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return MLA_ERR_INVALID_ARG;
+  const size_t need = mla::prefill_workspace_bytes(B, d->n_heads, s_cap);
+  if (ws_bytes < need) return MLA_ERR_WORKSPACE;
+  mla::PrefillArgs a{};
+  a.B = B;
+  a.H = d->n_heads;
+  a.T = T;
+  a.page_size_log2 = log2_exact(d->page_size);
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.s_cap = static_cast<int>(s_cap);
+  a.s_pad = static_cast<int>(mla::prefill_s_pad(s_cap));
+  a.max_q_len = max_q_len;
+  a.q_tiles = (max_q_len + mla::kPfQTile - 1) / mla::kPfQTile;
+  a.scale_log2 = static_cast<float>(static_cast<double>(d->softmax_scale) * 1.4426950408889634);
+  a.rope_base = d->rope_base;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.q_start = q_start;
+  a.pool = static_cast<const uint16_t*>(pool);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  char* ws = static_cast<char*>(workspace);
+  a.kn = reinterpret_cast<uint16_t*>(ws);
+  a.vt = reinterpret_cast<uint16_t*>(ws + need / 2);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_prof.active && 2 * g_prof.used + 1 < static_cast<int>(g_prof.ev.size())) {
+    e0 = g_prof.ev[2 * g_prof.used];
+    e1 = g_prof.ev[2 * g_prof.used + 1];
+    ++g_prof.used;
+  }
+  return from_hip(mla::launch_prefill(a, static_cast<hipStream_t>(stream), nullptr, nullptr, e0, e1));
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* d, const void* o_lat, const void* w_uv, int32_t B,

@@ -195,3 +195,37 @@ def test_project_append_validation():
     _expect(call(ws=P + 16), _native.MLA_ERR_INVALID_ARG)        # workspace not 256-aligned
     _expect(call(h=None), _native.MLA_ERR_INVALID_ARG)
     assert call(T=0) == _native.MLA_OK                           # no tokens: nothing enqueued
+
+
+def test_prefill_validation():
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    f = lib.mla_prefill_paged
+    B, mp = 2, 4
+    need = lib.mla_prefill_workspace_size(ctypes.byref(d), B, mp)
+    # K_nope and V^T: B * H * 128 tokens-padded-to-32 bf16 each
+    assert need == 2 * B * 128 * 128 * (mp * 64) * 2
+    p16 = mla.make_dims(4, 512, 64, 128, 128, 16)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(p16), 1, 3) == 2 * 4 * 128 * 64 * 2  # 48 -> 64
+    tiny = mla.make_dims(4, 32, 16, 16, 16, 16)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(tiny), B, mp) == 0
+    d8 = mla.make_dims(128, 512, 64, 128, 128, 64, fp8=True)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d8), B, mp) == 0
+
+    def call(dims=d, T=16, mq=16, qn=P, ws=P, wsb=need, B=B, lse=None, qs=P):
+        return f(ctypes.byref(dims), qn, P, qs, T, mq, P, P, mp, 40, P, B, P, P, ws, wsb, P, lse,
+                 None)
+
+    _expect(call(dims=tiny), _native.MLA_ERR_UNSUPPORTED)
+    _expect(call(dims=d8), _native.MLA_ERR_UNSUPPORTED)
+    _expect(call(T=-1), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(mq=-1), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(B=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(qn=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(qs=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(qn=P + 8), _native.MLA_ERR_INVALID_ARG)          # q_nope not 16-byte aligned
+    _expect(call(lse=P + 2), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(ws=P + 16), _native.MLA_ERR_INVALID_ARG)         # workspace not 256-aligned
+    _expect(call(wsb=need - 1), _native.MLA_ERR_WORKSPACE)
+    _expect(call(mq=(1 << 24) + 1), _native.MLA_ERR_UNSUPPORTED)
+    assert call(T=0) == _native.MLA_OK                            # nothing to do
+    assert call(mq=0) == _native.MLA_OK
