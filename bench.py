@@ -51,9 +51,11 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time the step as a captured HIP graph (replays) instead of eager calls; "
                          "the eager pass still runs for the split kernel's timing")
-    ap.add_argument("--op", default="step", choices=["step", "project_append"],
+    ap.add_argument("--op", default="step", choices=["step", "project_append", "prefill"],
                     help="step: the decode step (default); project_append: mla_project_append "
-                         "alone for one decode step's new tokens (B=64, d_model=7168, V3 rows)")
+                         "alone for one decode step's new tokens (B=64, d_model=7168, V3 rows); "
+                         "prefill: mla_prefill_paged on a 4096-token chunk of two 8192-token "
+                         "sequences (V3 heads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three device-to-device copies of MIB MiB (a kernel of known "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -155,6 +157,100 @@ def bench_project_append(args):
     }), flush=True)
 
 
+def bench_prefill(args):
+    """mla_prefill_paged on the second 4096-token chunk of two 8192-token
+    sequences (DeepSeek-V3 heads: H=128, latent 512, RoPE 64, K/V width 128;
+    page 64, permuted pages): the up-projection of all 8192 cached rows per
+    sequence to K_nope and V, then causal attention of the 4096 new tokens.
+    The roof is the bf16 MFMA rate: the attention kernel's algorithmic FLOPs
+    (each new token against the keys at positions <= its own) per launch over
+    its duration (HIP events on the launch stream)."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_nope_amd as mla
+    from workload import configs, make_inputs
+    from workload.torch_io import to_device
+
+    wl = configs.V3.with_(name="v3prefill", batch=2, seq_len=8192, q_len=4096)
+    B, S, n, H = wl.batch, wl.seq_len, wl.q_len, wl.n_heads
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    d = mla.make_dims(H, wl.d_c, wl.d_rope, wl.d_nope, wl.d_v, wl.page_size,
+                      softmax_scale=wl.softmax_scale, rope_base=wl.rope_base)
+    inp = make_inputs(wl)
+    t = to_device(inp, dev)
+    pool, _ = mla.new_pool(d, inp.num_pages, dev)
+    mla.append_latent(d, t["c_kv"], t["k_pe"], t["positions"], t["seq_ids"], t["block_table"], pool, None)
+    qn = t["q_nope"].reshape(B * n, H, wl.d_nope).contiguous()
+    qp = t["q_pe"].reshape(B * n, H, wl.d_rope).contiguous()
+    q_start = torch.tensor([0, n, 2 * n], dtype=torch.int32, device=dev)
+    ws = torch.empty(mla.prefill_workspace_size(d, B, inp.max_pages), dtype=torch.uint8, device=dev)
+    out = torch.empty((B * n, H, wl.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B * n, H), dtype=torch.float32, device=dev)
+    call = lambda: mla.prefill_paged(d, qn, qp, q_start, n, pool, t["block_table"], t["seq_lens"],
+                                     t["w_uk"], t["w_uv"], ws, out, lse)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mla.profile_begin(args.steps)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    attn_ms, n_rec = mla.profile_end()
+    ms = e0.elapsed_time(e1) / args.steps
+    attn_us = attn_ms / max(1, n_rec) * 1e3
+    # new token i sits at position S - n + i and sees S - n + i + 1 keys
+    keys = n * (S - n) + n * (n + 1) // 2
+    attn_flops = 2.0 * B * H * keys * (wl.d_nope + wl.d_rope + wl.d_v)
+    up_flops = 2.0 * B * S * wl.d_c * (wl.d_nope + wl.d_v) * H
+    tflops = attn_flops / (attn_us * 1e-6) / 1e12
+    line = {
+        "metric": "MLA explicit-form prefill tokens/s (chunk of 4096 new tokens on 8192-token "
+                  "sequences, H=128)",
+        "value": round(B * n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "V3 prefill chunk: B=2, S=8192, 4096 new tokens each (the second "
+                               "chunk), H=128, d_c=512, d_rope=64, d_nope=d_v=128, page 64, "
+                               "permuted pages",
+                   "kernels": "k_up (K_nope and V^T of all cached rows) + k_prefill (causal attention)",
+                   "up_projection_us": round(ms * 1e3 - attn_us, 2), "attention_us": round(attn_us, 2),
+                   "attention_flops": attn_flops, "up_projection_flops": up_flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "k_prefill",
+                     "note": "algorithmic FLOPs of the attention per launch / its mean duration "
+                             "(HIP events on the launch stream)"},
+    }
+    if args.cpu_sample > 0:
+        line["cpu_baseline"] = cpu_baseline_prefill(inp)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_prefill(inp):
+    """The oracle's explicit-form prefill on a bounded sample: sequence 0,
+    4 of 128 heads, 256 new tokens spread evenly over the chunk.  Scaled to
+    tokens/s of the whole workload as (rows * heads / H) / time."""
+    import numpy as np
+
+    from oracle import reference_prefill
+    wl = inp.wl
+    heads = [0, 42, 85, 127]
+    rows = list(np.linspace(0, wl.q_len - 1, 256).astype(int))
+    t0 = time.perf_counter()
+    reference_prefill(inp, batches=[0], heads=heads, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) * len(heads) / wl.n_heads / dt, 3), "unit": "tokens/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"sequence 0, heads {heads}, {len(rows)} of the {wl.q_len} new tokens "
+                      f"(evenly spaced), {dt:.1f} s"}
+
+
 def cpu_baseline(inp, n_seq: int):
     """Time the oracle (explicit fp64 form) on the first n_seq sequences."""
     import numpy as np
@@ -235,6 +331,9 @@ def main():
         sys.exit(2)
     if args.op == "project_append":
         bench_project_append(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
 
     import numpy as np

@@ -21,8 +21,8 @@
 //              so both stores are 64-byte runs).
 //   k_prefill  one workgroup of four waves per (sequence, head, 128 new
 //              tokens); each wave owns 32 queries.  Keys stream in 32-token
-//              tiles through a two-slot LDS ring filled by global->LDS copies
-//              one tile ahead.  The score tile is computed transposed,
+//              tiles through a four-slot LDS ring filled by global->LDS
+//              copies three tiles ahead.  The score tile is computed transposed,
 //              S^T = K . Q^T (32x32x16 bf16 MFMA, Q in registers), so each
 //              lane holds 16 keys of one query: the online-softmax row max
 //              needs one cross-half exchange, and P^T goes straight from the
@@ -139,6 +139,17 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
 // K_rope [32][64] (chunk c at c ^ (r mod 8)), V^T [128][32] (chunk c of row j
 // at c ^ ((j / 4) mod 4)).
 constexpr int kSlotKn = 0, kSlotKr = 8192, kSlotVt = 12288, kSlotBytes = 20480;
+constexpr int kAhead = 3;                   // key tiles in flight while one is computed
+constexpr int kSlots = kAhead + 1;          // ring slots (80 KB)
+constexpr int kCopiesPerTile = 5;           // global->LDS copies per wave per tile
+
+// s_waitcnt vmcnt(5 k): all but this wave's copies of its k most recently
+// issued tiles have landed
+__device__ __forceinline__ void wait_tiles_behind(int k) {
+  if (k >= 2) wait_vmcnt<2 * kCopiesPerTile>();
+  else if (k == 1) wait_vmcnt<kCopiesPerTile>();
+  else wait_vmcnt<0>();
+}
 
 #pragma clang fp contract(off)
 // RoPE pair (x0, x1) at angle pos * base^(-2i / 64): angle, sine, cosine and
@@ -158,8 +169,8 @@ __device__ __forceinline__ void rope_pair64(float x0, float x1, int i, int pos, 
 }
 #pragma clang fp contract(on)
 
-__global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kSlotBytes];   // 40 KB
+__global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlotBytes];   // 80 KB
   const int QT = a.q_tiles;
   const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
   const int u = 8 * (slot / QT) + xcd;                 // (sequence, head) unit
@@ -171,7 +182,8 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
   const int nc = min(n, a.max_q_len);                  // new tokens computed
   if (kPfQTile * qt >= nc) return;
   const int S = seq_tokens(a, b);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar registers
   const int r = lane & 31, half = lane >> 5;
 
   // keys the workgroup needs: up to the position of its last new token
@@ -216,7 +228,11 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     for (int s = 0; s < 12; ++s) qv[s] = zero;
   }
 
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  // block-table row read with scalar loads (the tile's page ids are
+  // wave-uniform), so waiting for them never waits for the copies in flight
+  const auto* bt = (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
+                   static_cast<int64_t>(b) * a.max_pages;
+  const int lg = a.page_size_log2;
   const uint16_t* kn_b = a.kn + static_cast<int64_t>(b) * a.s_pad * a.H * kPfDh;
   const uint16_t* vt_bh = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * a.s_pad;
   // copies of key tile nt into slot base: 8 K_nope, 4 K_rope and 8 V^T copies
@@ -232,11 +248,18 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
                   lds_addr(base + kSlotKn + 1024 * k));
     }
     {
+      // this wave's 8 key rows lie in at most two pages (pages hold >= 16 tokens)
       const int kr = 8 * wave + (lane >> 3);
       const int lc = (lane & 7) ^ (kr & 7);
       const int t = t0 + kr < S ? t0 + kr : S - 1;
-      lds_dma16_v(a.pool + pool_row(bt, t, a.page_size_log2, a.num_pages) * kPfRow + kPfDc + 8 * lc,
-                  lds_addr(base + kSlotKr + 1024 * wave));
+      const int ta = t0 + 8 * wave < S ? t0 + 8 * wave : S - 1;
+      const int tz = t0 + 8 * wave + 7 < S ? t0 + 8 * wave + 7 : S - 1;
+      int pa = bt[ta >> lg], pz = bt[tz >> lg];
+      if (static_cast<unsigned>(pa) >= static_cast<unsigned>(a.num_pages)) pa = 0;
+      if (static_cast<unsigned>(pz) >= static_cast<unsigned>(a.num_pages)) pz = 0;
+      const int page = (t >> lg) == (ta >> lg) ? pa : pz;
+      const int64_t prow = (static_cast<int64_t>(page) << lg) + (t & ((1 << lg) - 1));
+      lds_dma16_v(a.pool + prow * kPfRow + kPfDc + 8 * lc, lds_addr(base + kSlotKr + 1024 * wave));
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -250,14 +273,15 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
 
   float m = kNegInf, l = 0.f;
   f32x16 o[4] = {};
-  if (NT > 0) issue(0, lds);
+  for (int k = 0; k < kAhead && k < NT; ++k) issue(k, lds + k * kSlotBytes);
   for (int nt = 0; nt < NT; ++nt) {
-    wait_vmcnt<0>();
-    __syncthreads();                       // tile nt landed; slot (nt + 1) % 2 is free
-    if (nt + 1 < NT) issue(nt + 1, lds + ((nt + 1) & 1) * kSlotBytes);
+    // tiles nt + 1 .. nt + kAhead - 1 may still be in flight
+    wait_tiles_behind(min(kAhead - 1, NT - 1 - nt));
+    __syncthreads();                       // tile nt landed everywhere; the slot of tile nt - 1 is free
+    if (nt + kAhead < NT) issue(nt + kAhead, lds + ((nt + kAhead) % kSlots) * kSlotBytes);
     const int t0 = kPfKTile * nt;
     if (t0 > pw) continue;                 // every key of the tile is after this wave's queries
-    const char* sb = lds + (nt & 1) * kSlotBytes;
+    const char* sb = lds + (nt % kSlots) * kSlotBytes;
 
     // S^T tile: acc[e] is key t0 + 8 (e/4) + 4 half + e%4 of query r
     f32x16 sacc = {};
@@ -295,10 +319,12 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
       ls += p;
     }
     l = l * alpha + ls;
+    if (__any(alpha != 1.f)) {             // rescale only when some row max moved
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
+        for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
+    }
 
     // O^T += V^T . P^T over the 32 keys in two 16-key steps; step s2 uses the
     // keys {16 s2 + 4 half + [0,4), 16 s2 + 8 + 4 half + [0,4)} on both sides
