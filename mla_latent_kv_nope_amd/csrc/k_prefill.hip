@@ -52,6 +52,15 @@ __device__ __forceinline__ int seq_tokens(const PrefillArgs& a, int b) {
   return s < 0 ? 0 : (s > a.s_cap ? a.s_cap : s);
 }
 
+// V^T keeps each aligned 32-token block in the order the P.V product reads
+// it: 16-byte chunk 2 s + g holds the keys 16 s + 4 g + [0, 4) and
+// 16 s + 8 + 4 g + [0, 4), i.e. token k = 16 s + 8 e + 4 g + i sits at
+// slot 8 (2 s + g) + 4 e + i.
+__device__ __forceinline__ int vt_slot(int k) {
+  const int s = k >> 4, e = (k >> 3) & 1, g = (k >> 2) & 1, i = k & 3;
+  return 8 * (2 * s + g) + 4 * e + i;
+}
+
 // ---------------------------------------------------------------------------
 // Up-projection
 // ---------------------------------------------------------------------------
@@ -119,13 +128,15 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
               f32_to_bf16_bits(acc[ct][i]);
         }
     } else {
-      // acc[ct][i]: column n0 + 32 ct + 8 (i/4) + 4 half + i%4, token t0 + r
+      // acc[ct][i]: column n0 + 32 ct + 8 (i/4) + 4 half + i%4, token t0 + r,
+      // stored at slot vt_slot(r) of its 32-token block
+      const int slot = vt_slot(r);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int col = n0 + 32 * ct + 8 * (i >> 2) + 4 * half + (i & 3);
-          a.vt[((static_cast<int64_t>(b) * a.H + h) * kPfDh + col) * a.s_pad + t0 + r] =
+          a.vt[((static_cast<int64_t>(b) * a.H + h) * kPfDh + col) * a.s_pad + t0 + slot] =
               f32_to_bf16_bits(acc[ct][i]);
         }
     }
@@ -136,8 +147,8 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
 // Attention
 // ---------------------------------------------------------------------------
 // One ring slot: K_nope [32][128] (chunk c of key row r at c ^ (r mod 16)),
-// K_rope [32][64] (chunk c at c ^ (r mod 8)), V^T [128][32] (chunk c of row j
-// at c ^ ((j / 4) mod 4)).
+// K_rope [32][64] (chunk c at c ^ (r mod 8)), V^T [128][32] in vt_slot order
+// (chunk c of row j at c ^ ((j / 4) mod 4)).
 constexpr int kSlotKn = 0, kSlotKr = 8192, kSlotVt = 12288, kSlotBytes = 20480;
 constexpr int kAhead = 3;                   // key tiles in flight while one is computed
 constexpr int kSlots = kAhead + 1;          // ring slots (80 KB)
@@ -197,6 +208,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
   const int pos = i < nc ? S - n + i : -1;
   const int wlast = min(kPfQTile * qt + 32 * wave + 31, nc - 1);
   const int pw = kPfQTile * qt + 32 * wave < nc ? S - n + wlast : -1;   // wave's last position
+  const int pfirst = S - n + kPfQTile * qt + 32 * wave;                    // and its first
 
   // Q as the B operand: step s < 8 holds q_nope[16 s + 8 half, +8), steps
   // 8..11 the rotated q_pe[16 (s - 8) + 8 half, +8) (pairs 8 (s - 8) + 4 half + e)
@@ -296,17 +308,21 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
       sacc = mfma32(kv, qv[8 + s], sacc);
     }
 
-    // online softmax in base 2; masked keys are -inf, and a query that has
-    // seen no key yet keeps m = -inf with offset 0 (so p = 0, not NaN)
+    // online softmax in base 2 (m is the running max of scale * log2(e) *
+    // score); keys after a query's position are -inf, which only tiles
+    // reaching past the wave's first position need; a query that has seen no
+    // key yet keeps m = -inf with offset 0 (so p = 0, not NaN)
+    if (t0 + kPfKTile - 1 > pfirst) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = t0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        sacc[e] = key <= pos ? sacc[e] : kNegInf;
+      }
+    }
     float tmax = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = t0 + 8 * (e >> 2) + 4 * half + (e & 3);
-      const float x = key <= pos ? sacc[e] * a.scale_log2 : kNegInf;
-      sacc[e] = x;
-      tmax = fmaxf(tmax, x);
-    }
-    tmax = max_across_half_waves(tmax);
+    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
+    tmax = max_across_half_waves(tmax) * a.scale_log2;
     const float mn = fmaxf(m, tmax);
     const float mu = mn == kNegInf ? 0.f : mn;
     const float alpha = __builtin_amdgcn_exp2f(m - mu);
@@ -314,7 +330,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
     float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sacc[e] - mu);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, -mu));
       sacc[e] = p;
       ls += p;
     }
@@ -338,11 +354,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int j = 32 * cb + r;
-        const char* vrow = sb + kSlotVt + j * 64 + 8 * half;
-        const int sw = (j >> 2) & 3;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * ((2 * s2) ^ sw));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * ((2 * s2 + 1) ^ sw));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(sb + kSlotVt + j * 64 +
+                                                           16 * ((2 * s2 + half) ^ ((j >> 2) & 3)));
         o[cb] = mfma32(va, pb, o[cb]);
       }
     }
