@@ -76,12 +76,14 @@ def copy_calibration(mib: int):
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per k_split launch from the committed FETCH_SIZE / WRITE_SIZE
+    """HBM bytes per launch of the workload's main kernel (k_split, or
+    k_prefill for v3prefill) from the committed FETCH_SIZE / WRITE_SIZE
     summary, or None when the kernel sources changed since it was taken or
     the workload differs."""
     import hashlib
     import re
-    name = {"v3": "k_split_v3_b64_s8192.md", "v3mtp2": "k_split_v3mtp2_b64_q2_s8192.md"}.get(workload)
+    name = {"v3": "k_split_v3_b64_s8192.md", "v3mtp2": "k_split_v3mtp2_b64_q2_s8192.md",
+            "v3prefill": "k_prefill_v3_b2_s8192_c4096.md"}.get(workload)
     if name is None:
         return None
     path = os.path.join(ROOT, "profiles", name)
@@ -223,7 +225,7 @@ def bench_prefill(args):
                    "attention_flops": attn_flops, "up_projection_flops": up_flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "k_prefill",
+                     "traffic": measured_traffic("v3prefill"), "kernel": "k_prefill",
                      "note": "algorithmic FLOPs of the attention per launch / its mean duration "
                              "(HIP events on the launch stream)"},
     }
@@ -234,21 +236,19 @@ def bench_prefill(args):
 
 def cpu_baseline_prefill(inp):
     """The oracle's explicit-form prefill on a bounded sample: sequence 0,
-    4 of 128 heads, 256 new tokens spread evenly over the chunk.  Scaled to
-    tokens/s of the whole workload as (rows * heads / H) / time."""
-    import numpy as np
-
+    every second head (64 of 128), all 4096 new tokens.  Scaled to tokens/s
+    of the whole workload as (rows * heads / H) / time."""
     from oracle import reference_prefill
     wl = inp.wl
-    heads = [0, 42, 85, 127]
-    rows = list(np.linspace(0, wl.q_len - 1, 256).astype(int))
+    heads = list(range(0, wl.n_heads, 2))
+    rows = list(range(wl.q_len))
     t0 = time.perf_counter()
     reference_prefill(inp, batches=[0], heads=heads, rows=rows)
     dt = time.perf_counter() - t0
     return {"value": round(len(rows) * len(heads) / wl.n_heads / dt, 3), "unit": "tokens/s",
             "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"sequence 0, heads {heads}, {len(rows)} of the {wl.q_len} new tokens "
-                      f"(evenly spaced), {dt:.1f} s"}
+            "sample": f"sequence 0, {len(heads)} of {wl.n_heads} heads (every second), all "
+                      f"{len(rows)} new tokens, {dt:.1f} s"}
 
 
 def cpu_baseline(inp, n_seq: int):
