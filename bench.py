@@ -167,7 +167,6 @@ def bench_prefill(args):
     The roof is the bf16 MFMA rate: the attention kernel's algorithmic FLOPs
     (each new token against the keys at positions <= its own) per launch over
     its duration (HIP events on the launch stream)."""
-    import numpy as np
     import torch
 
     import mla_latent_kv_nope_amd as mla

@@ -38,6 +38,7 @@ namespace mla {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLazy = 8.f;                // base-2 headroom of the softmax offset
 
 // Page row holding token t of a block-table row (ids outside the pool read
 // page 0: results are then unspecified but every access stays in bounds).
@@ -163,11 +164,11 @@ __device__ __forceinline__ void wait_tiles_behind(int k) {
 }
 
 #pragma clang fp contract(off)
-// RoPE pair (x0, x1) at angle pos * base^(-2i / 64): angle, sine, cosine and
-// the rotation in double precision, rounded once to fp32
-__device__ __forceinline__ void rope_pair64(float x0, float x1, int i, int pos, double base,
+// RoPE pair (x0, x1) at angle pos * theta (theta = base^(-2i / 64), computed
+// on the host): angle, sine, cosine and the rotation in double precision,
+// rounded once to fp32
+__device__ __forceinline__ void rope_pair64(float x0, float x1, double theta, int pos,
                                             float* y0, float* y1) {
-  const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(kPfDr));
   double s, c;
   sincos(static_cast<double>(pos) * theta, &s, &c);
   const double u = static_cast<double>(x0), v = static_cast<double>(x1);
@@ -228,8 +229,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) {
         float y0, y1;
         rope_pair64(bf16_bits_to_f32(static_cast<uint16_t>(w[e] & 0xffffu)),
-                    bf16_bits_to_f32(static_cast<uint16_t>(w[e] >> 16)), 8 * s + 4 * half + e, pos,
-                    a.rope_base, &y0, &y1);
+                    bf16_bits_to_f32(static_cast<uint16_t>(w[e] >> 16)),
+                    a.rope_theta[8 * s + 4 * half + e], pos, &y0, &y1);
         o[e] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
                (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
       }
@@ -323,7 +324,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
     tmax = max_across_half_waves(tmax) * a.scale_log2;
-    const float mn = fmaxf(m, tmax);
+    // the offset moves only when the row max rises by more than kLazy, so
+    // p <= 2^kLazy (exact in bf16 and the fp32 sums) and the rescale below is
+    // rare; the final division by the row sum cancels whatever offset is used
+    const float mn = tmax > m + kLazy ? tmax : m;
     const float mu = mn == kNegInf ? 0.f : mn;
     const float alpha = __builtin_amdgcn_exp2f(m - mu);
     m = mn;

@@ -350,7 +350,8 @@ mla_status_t mla_prefill_paged(const mla_dims_t* d, const void* q_nope, const vo
   a.max_q_len = max_q_len;
   a.q_tiles = (max_q_len + mla::kPfQTile - 1) / mla::kPfQTile;
   a.scale_log2 = static_cast<float>(static_cast<double>(d->softmax_scale) * 1.4426950408889634);
-  a.rope_base = d->rope_base;
+  for (int i = 0; i < mla::kPfDr / 2; ++i)
+    a.rope_theta[i] = std::pow(d->rope_base, -2.0 * i / static_cast<double>(mla::kPfDr));
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.q_start = q_start;

@@ -23,7 +23,7 @@ struct PrefillArgs {
   int max_q_len;      // new tokens computed per sequence (the first max_q_len)
   int q_tiles;        // ceil(max_q_len / kPfQTile)
   float scale_log2;   // softmax_scale * log2(e)
-  double rope_base;
+  double rope_theta[kPfDr / 2];   // RoPE angle per position of pair i: base^(-2i / d_rope)
   const uint16_t* q_nope;      // [T][H][128]
   const uint16_t* q_pe;        // [T][H][64], un-rotated
   const int32_t* q_start;      // [B + 1]
