@@ -12,11 +12,12 @@
 // token at position seq_lens[b] - n_b + i and attends to positions <= its own.
 //
 // Two kernels:
-//   k_up       one workgroup per (head, 64-column half, 1024 tokens), launched
-//              once for K and once for V:
-//              the [512 x 64] weight slice sits in LDS and is read with the
-//              gfx950 transpose read; the latent rows go from the paged pool
-//              straight into MFMA registers.  K_nope is written [t][h][128],
+//   k_up       one workgroup of four waves per (head, 1024 tokens), launched
+//              once for K and once for V: the head's [512 x 128] weight sits
+//              in LDS and is read with the gfx950 transpose read; each wave
+//              computes 32 tokens x 128 columns, its latent rows going from
+//              the paged pool straight into MFMA registers, the next half of
+//              the reduction loading while this half's MFMAs run.  K_nope is written [t][h][128],
 //              V transposed [h][128][t] (the MFMA operands are swapped for V,
 //              so both stores are 64-byte runs).
 //   k_prefill  one workgroup of four waves per (sequence, head, 128 new
@@ -67,47 +68,56 @@ __device__ __forceinline__ int vt_slot(int k) {
 // ---------------------------------------------------------------------------
 template <bool IS_V>
 __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
-  constexpr int WROW = 64 * 2;                                // bytes per slice row
-  __shared__ __attribute__((aligned(1024))) char wl[kPfDc * WROW];   // 64 KB
-  const int h = blockIdx.x >> 1;
-  const int n0 = 64 * (blockIdx.x & 1);
+  constexpr int WROW = kPfDh * 2;                             // bytes per weight row
+  __shared__ __attribute__((aligned(1024))) char wl[kPfDc * WROW];   // 128 KB
+  const int h = blockIdx.x;
   const int b = blockIdx.z;
   const int tb = blockIdx.y * kUpTokens;
   const int S = seq_tokens(a, b);
   if (tb >= S) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // weight slice [512][64]: chunk c of row k stored at c ^ 2 (k mod 4), so a
+  // W[h] [512][128]: chunk c of row k stored at c ^ 2 (k mod 4), so a
   // transpose read's 16-lane group touches 4 rows in distinct banks
-  const uint16_t* wsrc = (IS_V ? a.w_uv : a.w_uk) + static_cast<int64_t>(h) * kPfDc * kPfDh + n0;
-  for (int k = wave; k < kPfDc / 8; k += 4) {
-    const int r = 8 * k + (lane >> 3);
-    const int c = (lane & 7) ^ (2 * (r & 3));
+  const uint16_t* wsrc = (IS_V ? a.w_uv : a.w_uk) + static_cast<int64_t>(h) * kPfDc * kPfDh;
+  for (int k = wave; k < kPfDc / 4; k += 4) {
+    const int r = 4 * k + (lane >> 4);
+    const int c = (lane & 15) ^ (2 * (r & 3));
     lds_dma16_v(wsrc + r * kPfDh + 8 * c, lds_addr(wl + 1024 * k));
   }
-  wait_vmcnt<0>();
-  __syncthreads();
 
   const int r = lane & 31, half = lane >> 5;
   const int G = lane >> 4, rr = (lane & 15) >> 2, q = lane & 3;
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
   const int tend = tb + kUpTokens < S ? tb + kUpTokens : S;
-  for (int t0 = tb + 32 * wave; t0 < tend; t0 += 128) {
-    // latent row of token t0 + r (rows past the sequence repeat its last
-    // token, so every 32-token block the attention reads holds finite values)
+  // latent row of token t0 + r (rows past the sequence repeat its last
+  // token, so every 32-token block the attention reads holds finite values)
+  auto row_of = [&](int t0) {
     const int t = t0 + r < S ? t0 + r : S - 1;
-    const uint16_t* crow = a.pool + pool_row(bt, t, a.page_size_log2, a.num_pages) * kPfRow + 8 * half;
-    f32x16 acc[2] = {};
+    return a.pool + pool_row(bt, t, a.page_size_log2, a.num_pages) * kPfRow + 8 * half;
+  };
+  // the two 256-element halves of the reduction go through alternate
+  // register sets, the next half's loads in flight during this half's MFMAs
+  bf16x8 av0[16], av1[16];
+  int t0 = tb + 32 * wave;
+  if (t0 < tend) {
+    const uint16_t* crow = row_of(t0);
 #pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-      bf16x8 av[16];
+    for (int s = 0; s < 16; ++s) av0[s] = *reinterpret_cast<const bf16x8*>(crow + 16 * s);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (; t0 < tend; t0 += 32 * 4) {
+    const uint16_t* crow = row_of(t0);
 #pragma unroll
-      for (int s = 0; s < 16; ++s) av[s] = *reinterpret_cast<const bf16x8*>(crow + 16 * (16 * hp + s));
+    for (int s = 0; s < 16; ++s) av1[s] = *reinterpret_cast<const bf16x8*>(crow + 256 + 16 * s);
+    f32x16 acc[4] = {};
+    auto half_pass = [&](const bf16x8* av, int hp) {
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int row = 16 * (16 * hp + s) + 8 * half + rr;     // row % 4 == rr
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < 4; ++ct) {
           const int col0 = 32 * ct + 16 * (G & 1) + 4 * q;
           const int cb = ((col0 >> 3) ^ (2 * rr)) * 16 + (col0 & 7) * 2;
           const bf16x4 lo = lds_read_tr16(wl + row * WROW + cb);
@@ -117,26 +127,33 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
           else acc[ct] = mfma32(av[s], bv, acc[ct]);
         }
       }
-    }
-    if constexpr (!IS_V) {
-      // acc[ct][i]: token t0 + 8 (i/4) + 4 half + i%4, column n0 + 32 ct + r
+    };
+    half_pass(av0, 0);
+    if (t0 + 32 * 4 < tend) {
+      const uint16_t* nrow = row_of(t0 + 32 * 4);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int s = 0; s < 16; ++s) av0[s] = *reinterpret_cast<const bf16x8*>(nrow + 16 * s);
+    }
+    half_pass(av1, 1);
+    if constexpr (!IS_V) {
+      // acc[ct][i]: token t0 + 8 (i/4) + 4 half + i%4, column 32 ct + r
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int tok = t0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          a.kn[((static_cast<int64_t>(b) * a.s_pad + tok) * a.H + h) * kPfDh + n0 + 32 * ct + r] =
+          a.kn[((static_cast<int64_t>(b) * a.s_pad + tok) * a.H + h) * kPfDh + 32 * ct + r] =
               f32_to_bf16_bits(acc[ct][i]);
         }
     } else {
-      // acc[ct][i]: column n0 + 32 ct + 8 (i/4) + 4 half + i%4, token t0 + r,
+      // acc[ct][i]: column 32 ct + 8 (i/4) + 4 half + i%4, token t0 + r,
       // stored at slot vt_slot(r) of its 32-token block
       const int slot = vt_slot(r);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int col = n0 + 32 * ct + 8 * (i >> 2) + 4 * half + (i & 3);
+          const int col = 32 * ct + 8 * (i >> 2) + 4 * half + (i & 3);
           a.vt[((static_cast<int64_t>(b) * a.H + h) * kPfDh + col) * a.s_pad + t0 + slot] =
               f32_to_bf16_bits(acc[ct][i]);
         }
@@ -417,8 +434,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, hipEvent_t up0, h
   if (grid > 0x7fffffff || a.B > 65535) return hipErrorInvalidValue;
   const int ytiles = (a.s_cap + kUpTokens - 1) / kUpTokens;
   if (up0) (void)hipEventRecord(up0, s);
-  hipLaunchKernelGGL(k_up<false>, dim3(2 * a.H, ytiles, a.B), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_up<true>, dim3(2 * a.H, ytiles, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_up<false>, dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_up<true>, dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
   if (up1) (void)hipEventRecord(up1, s);
   if (at0) (void)hipEventRecord(at0, s);
   hipLaunchKernelGGL(k_prefill, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
