@@ -15,7 +15,7 @@
 //   k_up       one workgroup of four waves per (head, 1024 tokens), launched
 //              once for K and once for V: the head's [512 x 128] weight sits
 //              in LDS and is read with the gfx950 transpose read; each wave
-//              computes 32 tokens x 128 columns, its latent rows going from
+//              computes 64 tokens x 128 columns, its latent rows going from
 //              the paged pool straight into MFMA registers, the next half of
 //              the reduction loading while this half's MFMAs run.  K_nope is written [t][h][128],
 //              V transposed [h][128][t] (the MFMA operands are swapped for V,
@@ -96,26 +96,34 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
     const int t = t0 + r < S ? t0 + r : S - 1;
     return a.pool + pool_row(bt, t, a.page_size_log2, a.num_pages) * kPfRow + 8 * half;
   };
-  // the two 256-element halves of the reduction go through alternate
-  // register sets, the next half's loads in flight during this half's MFMAs
-  bf16x8 av0[16], av1[16];
-  int t0 = tb + 32 * wave;
-  if (t0 < tend) {
-    const uint16_t* crow = row_of(t0);
+  // each wave takes two 32-token blocks, so every weight operand read from
+  // LDS feeds two MFMAs; the reduction runs in four 128-element quarters
+  // through two alternating register sets, the next quarter's loads in
+  // flight during this quarter's MFMAs (the row pointers are formed once per
+  // block, so no wait for a page id ever waits for those loads)
+  constexpr int kStride = 4 * 64;                              // tokens per pass of the workgroup
+  bf16x8 qa[2][8], qb[2][8];
+  const uint16_t* crow[2];
+  auto load_q = [&](bf16x8 (*dst)[8], const uint16_t* const* rows, int qq) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) av0[s] = *reinterpret_cast<const bf16x8*>(crow + 16 * s);
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) dst[rb][s] = *reinterpret_cast<const bf16x8*>(rows[rb] + 128 * qq + 16 * s);
+  };
+  int t0 = tb + 64 * wave;
+  if (t0 < tend) {
+    crow[0] = row_of(t0);
+    crow[1] = row_of(t0 + 32);
+    load_q(qa, crow, 0);
   }
   wait_vmcnt<0>();
   __syncthreads();
-  for (; t0 < tend; t0 += 32 * 4) {
-    const uint16_t* crow = row_of(t0);
+  for (; t0 < tend; t0 += kStride) {
+    f32x16 acc[2][4] = {};
+    auto compute_q = [&](const bf16x8 (*av)[8], int qq) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) av1[s] = *reinterpret_cast<const bf16x8*>(crow + 256 + 16 * s);
-    f32x16 acc[4] = {};
-    auto half_pass = [&](const bf16x8* av, int hp) {
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int row = 16 * (16 * hp + s) + 8 * half + rr;     // row % 4 == rr
+      for (int s = 0; s < 8; ++s) {
+        const int row = 16 * (8 * qq + s) + 8 * half + rr;      // row % 4 == rr
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const int col0 = 32 * ct + 16 * (G & 1) + 4 * q;
@@ -123,40 +131,63 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
           const bf16x4 lo = lds_read_tr16(wl + row * WROW + cb);
           const bf16x4 hi = lds_read_tr16(wl + (row + 4) * WROW + cb);
           const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          if constexpr (IS_V) acc[ct] = mfma32(bv, av[s], acc[ct]);
-          else acc[ct] = mfma32(av[s], bv, acc[ct]);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            if constexpr (IS_V) acc[rb][ct] = mfma32(bv, av[rb][s], acc[rb][ct]);
+            else acc[rb][ct] = mfma32(av[rb][s], bv, acc[rb][ct]);
+          }
         }
       }
     };
-    half_pass(av0, 0);
-    if (t0 + 32 * 4 < tend) {
-      const uint16_t* nrow = row_of(t0 + 32 * 4);
-#pragma unroll
-      for (int s = 0; s < 16; ++s) av0[s] = *reinterpret_cast<const bf16x8*>(nrow + 16 * s);
+    load_q(qb, crow, 1);
+    compute_q(qa, 0);
+    load_q(qa, crow, 2);
+    compute_q(qb, 1);
+    load_q(qb, crow, 3);
+    compute_q(qa, 2);
+    if (t0 + kStride < tend) {
+      crow[0] = row_of(t0 + kStride);
+      crow[1] = row_of(t0 + kStride + 32);
+      load_q(qa, crow, 0);
     }
-    half_pass(av1, 1);
-    if constexpr (!IS_V) {
-      // acc[ct][i]: token t0 + 8 (i/4) + 4 half + i%4, column 32 ct + r
+    compute_q(qb, 3);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+    for (int rb = 0; rb < 2; ++rb) {
+      const int tblk = t0 + 32 * rb;
+      // a block that starts past the sequence is not stored (its rows may lie
+      // beyond the workspace's token capacity)
+      if (tblk >= tend) break;
+      if constexpr (!IS_V) {
+        // acc[rb][ct][i]: token tblk + 8 (i/4) + 4 half + i%4, column 32 ct + r;
+        // the lane's part of the address is in the base pointer, the rest is
+        // uniform
+        // (the stride is made opaque here so that its 64 multiples are formed
+        // at the stores in scalar registers, not hoisted out of the loop)
+        int64_t ts = static_cast<int64_t>(a.H) * kPfDh;                // token stride
+        __asm__ volatile("" : "+s"(ts));
+        uint16_t* kb = a.kn + ((static_cast<int64_t>(b) * a.s_pad + tblk) * a.H + h) * kPfDh +
+                       4 * half * ts + r;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = t0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          a.kn[((static_cast<int64_t>(b) * a.s_pad + tok) * a.H + h) * kPfDh + 32 * ct + r] =
-              f32_to_bf16_bits(acc[ct][i]);
-        }
-    } else {
-      // acc[ct][i]: column 32 ct + 8 (i/4) + 4 half + i%4, token t0 + r,
-      // stored at slot vt_slot(r) of its 32-token block
-      const int slot = vt_slot(r);
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+          for (int i = 0; i < 16; ++i)
+            kb[(8 * (i >> 2) + (i & 3)) * ts + 32 * ct] = f32_to_bf16_bits(acc[rb][ct][i]);
+      } else {
+        // acc[rb][ct][i]: column 32 ct + 8 (i/4) + 4 half + i%4, token tblk + r,
+        // stored at slot vt_slot(r) of its 32-token block; the lane's part of
+        // the address is in the base pointer, the rest is uniform
+        // (the stride is made opaque here so that its 64 multiples are formed
+        // at the stores in scalar registers, not hoisted out of the loop)
+        int64_t cs = a.s_pad;                                           // column stride
+        __asm__ volatile("" : "+s"(cs));
+        uint16_t* vb = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * cs + tblk +
+                       4 * half * cs + vt_slot(r);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int col = 32 * ct + 8 * (i >> 2) + 4 * half + (i & 3);
-          a.vt[((static_cast<int64_t>(b) * a.H + h) * kPfDh + col) * a.s_pad + t0 + slot] =
-              f32_to_bf16_bits(acc[ct][i]);
-        }
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            vb[(32 * ct + 8 * (i >> 2) + (i & 3)) * cs] = f32_to_bf16_bits(acc[rb][ct][i]);
+      }
     }
   }
 }
