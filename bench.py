@@ -189,8 +189,8 @@ def bench_prefill(args):
     ws = torch.empty(mla.prefill_workspace_size(d, B, inp.max_pages), dtype=torch.uint8, device=dev)
     out = torch.empty((B * n, H, wl.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B * n, H), dtype=torch.float32, device=dev)
-    call = lambda: mla.prefill_paged(d, qn, qp, q_start, n, pool, t["block_table"], t["seq_lens"],
-                                     t["w_uk"], t["w_uv"], ws, out, lse)
+    call = lambda: mla.prefill_paged(d, qn, qp, q_start, n, pool, None, t["block_table"],
+                                     t["seq_lens"], t["w_uk"], t["w_uv"], ws, out, lse)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()

@@ -152,8 +152,9 @@ mla_status_t mla_project_append(const mla_dims_t* dims, int32_t d_model, const v
 /*
  * mla_prefill_workspace_size - bytes of device workspace mla_prefill_paged
  * needs for B sequences whose block-table rows hold max_pages pages: the
- * per-head K_nope and V of every addressable token, bf16,
- * 2 * B * n_heads * 128 * round_up(max_pages * page_size, 32) * 2 bytes.
+ * per-head K_nope and V of every addressable token and the shared RoPE keys,
+ * bf16: with P = round_up(max_pages * page_size, 32), two 256-byte aligned
+ * blocks of B * n_heads * 128 * P * 2 bytes and one of B * 64 * P * 2 bytes.
  * Returns 0 for unsupported dims, B <= 0 or max_pages <= 0.
  */
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t B, int32_t max_pages);
@@ -181,8 +182,9 @@ size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t B, int32_t max
  *   max_q_len   host bound on n_b: only the first max_q_len new tokens of a
  *               longer chunk are computed (the others are neither read nor
  *               written; positions still follow from n_b)
- *   pool, block_table, max_pages, num_pages, seq_lens: as for
- *               mla_decode_paged (bf16 cache only)
+ *   pool, scales, block_table, max_pages, num_pages, seq_lens: as for
+ *               mla_decode_paged (an fp8 cache is dequantised as code * scale
+ *               rounded to bf16, as in decode)
  *   w_uk, w_uv  bf16 [H][d_c][d_nope] and [H][d_c][d_v]
  *   workspace   >= mla_prefill_workspace_size() bytes, 256-byte aligned
  *   out         bf16 [T][H][d_v] (written): sum_t p_t V_h[t]
@@ -190,14 +192,14 @@ size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t B, int32_t max
  * with s_t = softmax_scale * (q_nope . K_h[t] + RoPE(q_pe) . k_rot[t]).
  * K and V are rounded to bf16 in the workspace, scores and the softmax are
  * fp32, P is rounded to bf16 for the P.V product.  Supported for d_c 512,
- * d_rope 64, d_nope = d_v = 128 and a bf16 cache (else MLA_ERR_UNSUPPORTED).
+ * d_rope 64 and d_nope = d_v = 128 (else MLA_ERR_UNSUPPORTED).
  * Rows outside [0, T) are neither read nor written.  T == 0 or
  * max_q_len == 0 is a no-op.
  */
 mla_status_t mla_prefill_paged(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
                                const int32_t* q_start, int32_t T, int32_t max_q_len,
-                               const void* pool, const int32_t* block_table, int32_t max_pages,
-                               int32_t num_pages, const int32_t* seq_lens, int32_t B,
+                               const void* pool, const float* scales, const int32_t* block_table,
+                               int32_t max_pages, int32_t num_pages, const int32_t* seq_lens, int32_t B,
                                const void* w_uk, const void* w_uv, void* workspace,
                                size_t ws_bytes, void* out, float* lse, void* stream);
 

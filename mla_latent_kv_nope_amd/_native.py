@@ -81,8 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_project_append.restype = ctypes.c_int
     lib.mla_prefill_workspace_size.argtypes = [_DP, _I, _I]
     lib.mla_prefill_workspace_size.restype = ctypes.c_size_t
-    lib.mla_prefill_paged.argtypes = [_DP, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _P, _P, _P,
-                                      ctypes.c_size_t, _P, _P, _P]
+    lib.mla_prefill_paged.argtypes = [_DP, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, _P,
+                                      _P, ctypes.c_size_t, _P, _P, _P]
     lib.mla_prefill_paged.restype = ctypes.c_int
     lib.mla_out_proj.argtypes = [_DP, _P, _P, _I, _P, _P]
     lib.mla_out_proj.restype = ctypes.c_int

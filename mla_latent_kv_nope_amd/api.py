@@ -281,10 +281,11 @@ def prefill_workspace_size(d: Dims, B: int, max_pages: int) -> int:
 
 
 def prefill_paged(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_start: torch.Tensor,
-                  max_q_len: int, pool: torch.Tensor, block_table: torch.Tensor,
-                  seq_lens: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
-                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                  lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+                  max_q_len: int, pool: torch.Tensor, scales: Optional[torch.Tensor],
+                  block_table: torch.Tensor, seq_lens: torch.Tensor, w_uk: torch.Tensor,
+                  w_uv: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  want_lse: bool = True):
     """mla_prefill_paged: q_nope [T][H][d_nope], q_pe [T][H][d_rope], q_start [B+1]
     (device int32); returns out [T][H][d_v] and lse [T][H] (or None)."""
     H = d.n_heads
@@ -297,8 +298,10 @@ def prefill_paged(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_start: to
     _req(q_start, "q_start", torch.int32, (B + 1,))
     num_pages = pool.shape[0]
     if _is_fp8(d):
-        raise ValueError("mla_prefill_paged reads a bf16 cache")
-    _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+        _req(pool, "pool", torch.uint8, pool_shape(d, num_pages))
+        _req(scales, "scales", torch.float32, (num_pages, d.page_size))
+    else:
+        _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B][max_pages]")
     _req(block_table, "block_table", torch.int32)
@@ -318,7 +321,8 @@ def prefill_paged(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_start: to
     if lse is not None:
         _req(lse, "lse", torch.float32, (T, H))
     st = lib.mla_prefill_paged(ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(q_start), T,
-                               int(max_q_len), _ptr(pool), _ptr(block_table), max_pages, num_pages,
+                               int(max_q_len), _ptr(pool), _ptr(scales), _ptr(block_table),
+                               max_pages, num_pages,
                                _ptr(seq_lens), B, _ptr(w_uk), _ptr(w_uv), _ptr(workspace),
                                workspace.numel(), _ptr(out), _ptr(lse), _stream())
     _check("mla_prefill_paged", st)

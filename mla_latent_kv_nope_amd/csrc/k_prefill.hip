@@ -32,6 +32,8 @@
 //   Workgroups of one (sequence, head) sit on one XCD (blockIdx mod 8), so
 //   their K/V tiles are shared through that XCD's L2; the query tiles that
 //   see the most keys start first.
+#include <type_traits>
+
 #include "mla_common.hpp"
 #include "prefill.hpp"
 
@@ -66,7 +68,7 @@ __device__ __forceinline__ int vt_slot(int k) {
 // ---------------------------------------------------------------------------
 // Up-projection
 // ---------------------------------------------------------------------------
-template <bool IS_V>
+template <bool IS_V, bool FP8>
 __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
   constexpr int WROW = kPfDh * 2;                             // bytes per weight row
   __shared__ __attribute__((aligned(1024))) char wl[kPfDc * WROW];   // 128 KB
@@ -90,11 +92,27 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
   const int G = lane >> 4, rr = (lane & 15) >> 2, q = lane & 3;
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
   const int tend = tb + kUpTokens < S ? tb + kUpTokens : S;
-  // latent row of token t0 + r (rows past the sequence repeat its last
-  // token, so every 32-token block the attention reads holds finite values)
+  // pool row of token t0 + r (rows past the sequence repeat its last token,
+  // so every 32-token block the attention reads holds finite values)
   auto row_of = [&](int t0) {
     const int t = t0 + r < S ? t0 + r : S - 1;
-    return a.pool + pool_row(bt, t, a.page_size_log2, a.num_pages) * kPfRow + 8 * half;
+    return pool_row(bt, t, a.page_size_log2, a.num_pages);
+  };
+  // Latent elements as loaded: 8 bf16 (16 bytes) or, for an fp8 cache, 8
+  // E4M3 codes (8 bytes) turned into bf16 as code * scale at the MFMA (the
+  // same rounding the fp8 decode applies)
+  using Raw = typename std::conditional<FP8, uint2, bf16x8>::type;
+  constexpr int ES = FP8 ? 1 : 2;                              // bytes per element
+  const char* pool = static_cast<const char*>(a.pool);
+  auto row_ptr = [&](int64_t prow) { return pool + (prow * kPfRow + 8 * half) * ES; };
+  auto to_bf16 = [&](const Raw& v, float sc) -> bf16x8 {
+    if constexpr (FP8) {
+      return __builtin_bit_cast(bf16x8, make_uint4(fp8x2_to_bf16x2<false>(v.x, sc), fp8x2_to_bf16x2<true>(v.x, sc),
+                                                   fp8x2_to_bf16x2<false>(v.y, sc), fp8x2_to_bf16x2<true>(v.y, sc)));
+    } else {
+      (void)sc;
+      return v;
+    }
   };
   // each wave takes two 32-token blocks, so every weight operand read from
   // LDS feeds two MFMAs; the reduction runs in four 128-element quarters
@@ -102,25 +120,37 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
   // flight during this quarter's MFMAs (the row pointers are formed once per
   // block, so no wait for a page id ever waits for those loads)
   constexpr int kStride = 4 * 64;                              // tokens per pass of the workgroup
-  bf16x8 qa[2][8], qb[2][8];
-  const uint16_t* crow[2];
-  auto load_q = [&](bf16x8 (*dst)[8], const uint16_t* const* rows, int qq) {
+  Raw qa[2][8], qb[2][8];
+  int64_t prow[2] = {0, 0};
+  float sc[2] = {1.f, 1.f};
+  auto load_q = [&](Raw (*dst)[8], int qq) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+      const char* base = row_ptr(prow[rb]);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) dst[rb][s] = *reinterpret_cast<const bf16x8*>(rows[rb] + 128 * qq + 16 * s);
+      for (int s = 0; s < 8; ++s) dst[rb][s] = *reinterpret_cast<const Raw*>(base + (128 * qq + 16 * s) * ES);
+    }
+  };
+  auto set_rows = [&](int tq) {
+    prow[0] = row_of(tq);
+    prow[1] = row_of(tq + 32);
+    if constexpr (FP8) {
+      sc[0] = a.scales[prow[0]];
+      sc[1] = a.scales[prow[1]];
+    }
   };
   int t0 = tb + 64 * wave;
   if (t0 < tend) {
-    crow[0] = row_of(t0);
-    crow[1] = row_of(t0 + 32);
-    load_q(qa, crow, 0);
+    set_rows(t0);
+    load_q(qa, 0);
   }
   wait_vmcnt<0>();
   __syncthreads();
   for (; t0 < tend; t0 += kStride) {
+    const int64_t prow_now[2] = {prow[0], prow[1]};
+    const float sc_now[2] = {sc[0], sc[1]};
     f32x16 acc[2][4] = {};
-    auto compute_q = [&](const bf16x8 (*av)[8], int qq) {
+    auto compute_q = [&](const Raw (*av)[8], int qq) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int row = 16 * (8 * qq + s) + 8 * half + rr;      // row % 4 == rr
@@ -133,22 +163,22 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
           const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            if constexpr (IS_V) acc[rb][ct] = mfma32(bv, av[rb][s], acc[rb][ct]);
-            else acc[rb][ct] = mfma32(av[rb][s], bv, acc[rb][ct]);
+            const bf16x8 x = to_bf16(av[rb][s], sc_now[rb]);
+            if constexpr (IS_V) acc[rb][ct] = mfma32(bv, x, acc[rb][ct]);
+            else acc[rb][ct] = mfma32(x, bv, acc[rb][ct]);
           }
         }
       }
     };
-    load_q(qb, crow, 1);
+    load_q(qb, 1);
     compute_q(qa, 0);
-    load_q(qa, crow, 2);
+    load_q(qa, 2);
     compute_q(qb, 1);
-    load_q(qb, crow, 3);
+    load_q(qb, 3);
     compute_q(qa, 2);
     if (t0 + kStride < tend) {
-      crow[0] = row_of(t0 + kStride);
-      crow[1] = row_of(t0 + kStride + 32);
-      load_q(qa, crow, 0);
+      set_rows(t0 + kStride);
+      load_q(qa, 0);
     }
     compute_q(qb, 3);
 #pragma unroll
@@ -158,6 +188,26 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
       // beyond the workspace's token capacity)
       if (tblk >= tend) break;
       if constexpr (!IS_V) {
+        // the RoPE key rows (shared by all heads) go to the workspace once,
+        // as bf16, from the head-0 workgroups: lane (r, half) moves elements
+        // [32 half, +32) of token tblk + r's rotated key
+        if (h == 0) {
+          uint4* dst = reinterpret_cast<uint4*>(a.kr + (static_cast<int64_t>(b) * a.s_pad + tblk + r) * kPfDr + 32 * half);
+          const char* src = pool + (prow_now[rb] * kPfRow + kPfDc + 32 * half) * ES;
+          if constexpr (FP8) {
+            const uint4 c0 = reinterpret_cast<const uint4*>(src)[0];
+            const uint4 c1 = reinterpret_cast<const uint4*>(src)[1];
+            const float f = sc_now[rb];
+            const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              dst[k] = make_uint4(fp8x2_to_bf16x2<false>(w[2 * k], f), fp8x2_to_bf16x2<true>(w[2 * k], f),
+                                  fp8x2_to_bf16x2<false>(w[2 * k + 1], f), fp8x2_to_bf16x2<true>(w[2 * k + 1], f));
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dst[k] = reinterpret_cast<const uint4*>(src)[k];
+          }
+        }
         // acc[rb][ct][i]: token tblk + 8 (i/4) + 4 half + i%4, column 32 ct + r;
         // the lane's part of the address is in the base pointer, the rest is
         // uniform
@@ -289,11 +339,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
     for (int s = 0; s < 12; ++s) qv[s] = zero;
   }
 
-  // block-table row read with scalar loads (the tile's page ids are
-  // wave-uniform), so waiting for them never waits for the copies in flight
-  const auto* bt = (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
-                   static_cast<int64_t>(b) * a.max_pages;
-  const int lg = a.page_size_log2;
+  const uint16_t* kr_b = a.kr + static_cast<int64_t>(b) * a.s_pad * kPfDr;
   const uint16_t* kn_b = a.kn + static_cast<int64_t>(b) * a.s_pad * a.H * kPfDh;
   const uint16_t* vt_bh = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * a.s_pad;
   // copies of key tile nt into slot base: 8 K_nope, 4 K_rope and 8 V^T copies
@@ -309,18 +355,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
                   lds_addr(base + kSlotKn + 1024 * k));
     }
     {
-      // this wave's 8 key rows lie in at most two pages (pages hold >= 16 tokens)
       const int kr = 8 * wave + (lane >> 3);
       const int lc = (lane & 7) ^ (kr & 7);
-      const int t = t0 + kr < S ? t0 + kr : S - 1;
-      const int ta = t0 + 8 * wave < S ? t0 + 8 * wave : S - 1;
-      const int tz = t0 + 8 * wave + 7 < S ? t0 + 8 * wave + 7 : S - 1;
-      int pa = bt[ta >> lg], pz = bt[tz >> lg];
-      if (static_cast<unsigned>(pa) >= static_cast<unsigned>(a.num_pages)) pa = 0;
-      if (static_cast<unsigned>(pz) >= static_cast<unsigned>(a.num_pages)) pz = 0;
-      const int page = (t >> lg) == (ta >> lg) ? pa : pz;
-      const int64_t prow = (static_cast<int64_t>(page) << lg) + (t & ((1 << lg) - 1));
-      lds_dma16_v(a.pool + prow * kPfRow + kPfDc + 8 * lc, lds_addr(base + kSlotKr + 1024 * wave));
+      lds_dma16_v(kr_b + static_cast<int64_t>(t0 + kr) * kPfDr + 8 * lc,
+                  lds_addr(base + kSlotKr + 1024 * wave));
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -445,16 +483,21 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
 
 }  // namespace
 
-bool prefill_supported(int d_c, int d_rope, int d_nope, int d_v, bool fp8) {
-  return d_c == kPfDc && d_rope == kPfDr && d_nope == kPfDh && d_v == kPfDh && !fp8;
+bool prefill_supported(int d_c, int d_rope, int d_nope, int d_v) {
+  return d_c == kPfDc && d_rope == kPfDr && d_nope == kPfDh && d_v == kPfDh;
 }
 
 int64_t prefill_s_pad(int64_t s_cap) { return (s_cap + kPfKTile - 1) / kPfKTile * kPfKTile; }
 
 size_t prefill_workspace_bytes(int B, int H, int64_t s_cap) {
   const size_t one = static_cast<size_t>(B) * H * kPfDh * prefill_s_pad(s_cap) * 2;
-  const size_t al = (one + 255) / 256 * 256;
-  return 2 * al;
+  const size_t rope = static_cast<size_t>(B) * kPfDr * prefill_s_pad(s_cap) * 2;
+  return 2 * ((one + 255) / 256 * 256) + (rope + 255) / 256 * 256;
+}
+
+size_t prefill_kv_bytes(int B, int H, int64_t s_cap) {
+  const size_t one = static_cast<size_t>(B) * H * kPfDh * prefill_s_pad(s_cap) * 2;
+  return (one + 255) / 256 * 256;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, hipEvent_t up0, hipEvent_t up1,
@@ -465,8 +508,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, hipEvent_t up0, h
   if (grid > 0x7fffffff || a.B > 65535) return hipErrorInvalidValue;
   const int ytiles = (a.s_cap + kUpTokens - 1) / kUpTokens;
   if (up0) (void)hipEventRecord(up0, s);
-  hipLaunchKernelGGL(k_up<false>, dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_up<true>, dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+  if (a.fp8) {
+    hipLaunchKernelGGL((k_up<false, true>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_up<true, true>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_up<false, false>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_up<true, false>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+  }
   if (up1) (void)hipEventRecord(up1, s);
   if (at0) (void)hipEventRecord(at0, s);
   hipLaunchKernelGGL(k_prefill, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);

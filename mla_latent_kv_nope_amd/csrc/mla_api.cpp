@@ -304,8 +304,7 @@ mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const vo
 
 size_t mla_prefill_workspace_size(const mla_dims_t* d, int32_t B, int32_t max_pages) {
   if (check_dims(d) != MLA_OK || B <= 0 || max_pages <= 0) return 0;
-  if (!mla::prefill_supported(d->d_c, d->d_rope, d->d_nope, d->d_v, d->cache_dtype == MLA_CACHE_FP8_E4M3))
-    return 0;
+  if (!mla::prefill_supported(d->d_c, d->d_rope, d->d_nope, d->d_v)) return 0;
   const int64_t s_cap = static_cast<int64_t>(max_pages) * d->page_size;
   if (s_cap > (int64_t{1} << 24)) return 0;
   return mla::prefill_workspace_bytes(B, d->n_heads, s_cap);
@@ -313,28 +312,31 @@ size_t mla_prefill_workspace_size(const mla_dims_t* d, int32_t B, int32_t max_pa
 
 mla_status_t mla_prefill_paged(const mla_dims_t* d, const void* q_nope, const void* q_pe,
                                const int32_t* q_start, int32_t T, int32_t max_q_len,
-                               const void* pool, const int32_t* block_table, int32_t max_pages,
+                               const void* pool, const float* scales, const int32_t* block_table,
+                               int32_t max_pages,
                                int32_t num_pages, const int32_t* seq_lens, int32_t B,
                                const void* w_uk, const void* w_uv, void* workspace,
                                size_t ws_bytes, void* out, float* lse, void* stream) {
   const mla_status_t st = check_dims(d);
   if (st != MLA_OK) return st;
   if (T < 0 || max_q_len < 0 || B <= 0 || max_pages <= 0 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
-  if (!mla::prefill_supported(d->d_c, d->d_rope, d->d_nope, d->d_v, d->cache_dtype == MLA_CACHE_FP8_E4M3))
-    return MLA_ERR_UNSUPPORTED;
+  if (!mla::prefill_supported(d->d_c, d->d_rope, d->d_nope, d->d_v)) return MLA_ERR_UNSUPPORTED;
+  const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
   const int64_t s_cap = static_cast<int64_t>(max_pages) * d->page_size;
   if (s_cap > (int64_t{1} << 24)) return MLA_ERR_UNSUPPORTED;
   if (B > 65535 || max_q_len > (1 << 24) ||
       (static_cast<int64_t>(B) * d->n_heads + 7) / 8 * 8 * ((max_q_len + mla::kPfQTile - 1) / mla::kPfQTile) >
           0x7fffffff)
     return MLA_ERR_UNSUPPORTED;
+  if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
   if (T == 0 || max_q_len == 0) return MLA_OK;
   if (!q_nope || !q_pe || !q_start || !pool || !block_table || !seq_lens || !w_uk || !w_uv ||
       !workspace || !out)
     return MLA_ERR_INVALID_ARG;
   if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(q_start, 4) || !aligned(pool, 16) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
-      !aligned(workspace, 256) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+      !aligned(workspace, 256) || !aligned(out, 16) || (lse && !aligned(lse, 4)) ||
+      (fp8 && !aligned(scales, 4)))
     return MLA_ERR_INVALID_ARG;
   const size_t need = mla::prefill_workspace_bytes(B, d->n_heads, s_cap);
   if (ws_bytes < need) return MLA_ERR_WORKSPACE;
@@ -355,14 +357,18 @@ mla_status_t mla_prefill_paged(const mla_dims_t* d, const void* q_nope, const vo
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.q_start = q_start;
-  a.pool = static_cast<const uint16_t*>(pool);
+  a.pool = pool;
+  a.scales = scales;
+  a.fp8 = fp8;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.w_uk = static_cast<const uint16_t*>(w_uk);
   a.w_uv = static_cast<const uint16_t*>(w_uv);
   char* ws = static_cast<char*>(workspace);
+  const size_t kv = mla::prefill_kv_bytes(B, d->n_heads, s_cap);
   a.kn = reinterpret_cast<uint16_t*>(ws);
-  a.vt = reinterpret_cast<uint16_t*>(ws + need / 2);
+  a.vt = reinterpret_cast<uint16_t*>(ws + kv);
+  a.kr = reinterpret_cast<uint16_t*>(ws + 2 * kv);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   hipEvent_t e0 = nullptr, e1 = nullptr;

@@ -27,21 +27,26 @@ struct PrefillArgs {
   const uint16_t* q_nope;      // [T][H][128]
   const uint16_t* q_pe;        // [T][H][64], un-rotated
   const int32_t* q_start;      // [B + 1]
-  const uint16_t* pool;        // [num_pages][page_size][576] bf16
+  const void* pool;            // [num_pages][page_size][576] bf16, or E4M3 codes
+  const float* scales;         // [num_pages][page_size] (fp8 cache), else nullptr
+  bool fp8;
   const int32_t* block_table;  // [B][max_pages]
   const int32_t* seq_lens;     // [B]
   const uint16_t* w_uk;        // [H][512][128]
   const uint16_t* w_uv;        // [H][512][128]
   uint16_t* kn;                // workspace [B][s_pad][H][128]: K_nope = C . W_UK[h]
   uint16_t* vt;                // workspace [B][H][128][s_pad]: V^T, V = C . W_UV[h]
+  uint16_t* kr;                // workspace [B][s_pad][64]: the rotated RoPE keys, bf16
   uint16_t* out;               // [T][H][128]
   float* lse;                  // [T][H] or nullptr
 };
 
-bool prefill_supported(int d_c, int d_rope, int d_nope, int d_v, bool fp8);
-// Workspace bytes (kn then vt, each 256-byte aligned) for B sequences whose
-// block-table rows address s_cap tokens.
+bool prefill_supported(int d_c, int d_rope, int d_nope, int d_v);
+// Workspace bytes (kn, vt, then kr, each 256-byte aligned) for B sequences
+// whose block-table rows address s_cap tokens; prefill_kv_bytes is the size
+// of each of kn and vt (the offsets of vt and kr).
 size_t prefill_workspace_bytes(int B, int H, int64_t s_cap);
+size_t prefill_kv_bytes(int B, int H, int64_t s_cap);
 int64_t prefill_s_pad(int64_t s_cap);
 // Launches the up-projection and the attention kernel on stream s.  Optional
 // event pairs bracket each of the two kernels (nullptr: none).

@@ -202,21 +202,24 @@ def test_prefill_validation():
     f = lib.mla_prefill_paged
     B, mp = 2, 4
     need = lib.mla_prefill_workspace_size(ctypes.byref(d), B, mp)
-    # K_nope and V^T: B * H * 128 tokens-padded-to-32 bf16 each
-    assert need == 2 * B * 128 * 128 * (mp * 64) * 2
+    # K_nope and V^T: B * H * 128 tokens-padded-to-32 bf16 each, then the
+    # RoPE keys B * 64 per token
+    assert need == 2 * B * 128 * 128 * (mp * 64) * 2 + B * 64 * (mp * 64) * 2
     p16 = mla.make_dims(4, 512, 64, 128, 128, 16)
-    assert lib.mla_prefill_workspace_size(ctypes.byref(p16), 1, 3) == 2 * 4 * 128 * 64 * 2  # 48 -> 64
+    assert lib.mla_prefill_workspace_size(ctypes.byref(p16), 1, 3) == \
+        2 * 4 * 128 * 64 * 2 + 64 * 64 * 2                                  # 48 -> 64 tokens
     tiny = mla.make_dims(4, 32, 16, 16, 16, 16)
     assert lib.mla_prefill_workspace_size(ctypes.byref(tiny), B, mp) == 0
     d8 = mla.make_dims(128, 512, 64, 128, 128, 64, fp8=True)
-    assert lib.mla_prefill_workspace_size(ctypes.byref(d8), B, mp) == 0
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d8), B, mp) == need
 
-    def call(dims=d, T=16, mq=16, qn=P, ws=P, wsb=need, B=B, lse=None, qs=P):
-        return f(ctypes.byref(dims), qn, P, qs, T, mq, P, P, mp, 40, P, B, P, P, ws, wsb, P, lse,
-                 None)
+    def call(dims=d, T=16, mq=16, qn=P, ws=P, wsb=need, B=B, lse=None, qs=P, sc=None):
+        return f(ctypes.byref(dims), qn, P, qs, T, mq, P, sc, P, mp, 40, P, B, P, P, ws, wsb, P,
+                 lse, None)
 
     _expect(call(dims=tiny), _native.MLA_ERR_UNSUPPORTED)
-    _expect(call(dims=d8), _native.MLA_ERR_UNSUPPORTED)
+    _expect(call(dims=d8), _native.MLA_ERR_INVALID_ARG)             # fp8 without scales
+    _expect(call(sc=P), _native.MLA_ERR_INVALID_ARG)                # scales with a bf16 cache
     _expect(call(T=-1), _native.MLA_ERR_INVALID_ARG)
     _expect(call(mq=-1), _native.MLA_ERR_INVALID_ARG)
     _expect(call(B=0), _native.MLA_ERR_INVALID_ARG)

@@ -23,9 +23,9 @@ pytestmark = pytest.mark.gpu
 V3D = dict(d_c=512, d_rope=64, d_nope=128, d_v=128)
 
 
-def _wl(name, heads, seq_lens, chunk, page_size=64):
+def _wl(name, heads, seq_lens, chunk, page_size=64, fp8=False):
     return configs.V3.with_(name=name, batch=len(seq_lens), n_heads=heads, seq_len=None,
-                            seq_lens=tuple(seq_lens), q_len=chunk, page_size=page_size)
+                            seq_lens=tuple(seq_lens), q_len=chunk, page_size=page_size, fp8=fp8)
 
 
 CASES = [
@@ -37,6 +37,9 @@ CASES = [
     _wl("v3_h3_prompt_p256", 3, (515,), 515, page_size=256),
     # V2-Lite head count
     configs.V2LITE.with_(name="v2lite_c200", batch=2, seq_len=None, seq_lens=(200, 1100), q_len=200),
+    # fp8 E4M3 cache with per-token scales (dequantised as in decode)
+    _wl("v3_fp8_h4_c150", 4, (150, 90, 1300), 150, fp8=True),
+    _wl("v3_fp8_h2_c64_p16", 2, (64, 33), 64, page_size=16, fp8=True),
 ]
 
 
@@ -53,8 +56,8 @@ def run_prefill(inp, d, n_new=None, cache=None):
     qp_p = torch.cat([qp[b, ql - n_new[b]:] for b in range(B)]).contiguous()
     starts = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
     q_start = torch.from_numpy(starts).to("cuda")
-    out, lse = mla.prefill_paged(d, qn_p, qp_p, q_start, max(n_new), pool, t["block_table"],
-                                 t["seq_lens"], t["w_uk"], t["w_uv"])
+    out, lse = mla.prefill_paged(d, qn_p, qp_p, q_start, max(n_new), pool, scales,
+                                 t["block_table"], t["seq_lens"], t["w_uk"], t["w_uv"])
     torch.cuda.synchronize()
     f = lambda x: x.float().cpu().numpy().astype(np.float64)
     return f(out), f(lse), starts, (pool, scales, t)
@@ -119,8 +122,8 @@ def test_rows_outside_the_chunk_are_untouched():
     qp = t["q_pe"].reshape(40, 2, 64).contiguous()
     q_start = torch.tensor([0, 40], dtype=torch.int32, device="cuda")
     out = torch.full((40, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda")
-    mla.prefill_paged(d, qn, qp, q_start, 32, pool, t["block_table"], t["seq_lens"], t["w_uk"],
-                      t["w_uv"], out=out, want_lse=False)
+    mla.prefill_paged(d, qn, qp, q_start, 32, pool, scales, t["block_table"], t["seq_lens"],
+                      t["w_uk"], t["w_uv"], out=out, want_lse=False)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64)
     assert np.all(o[32:] == 7.0)
