@@ -99,3 +99,50 @@ def test_captured_step_replays_bit_for_bit(wl):
         g.replay()
         torch.cuda.synchronize()
         assert same(snapshot(), eager2), f"replay {i} after the input update differs"
+
+
+def test_captured_prefill_replays_bit_for_bit():
+    """mla_prefill_paged (both up-projections and the attention) captured and
+    replayed, with eager work between replays: bit for bit the eager call."""
+    wl = configs.V3.with_(name="v3_prefill_graph", batch=2, n_heads=8, seq_len=None,
+                          seq_lens=(300, 700), q_len=200)
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    t = to_device(inp, DEV)
+    B, ql, H = wl.batch, wl.q_len, wl.n_heads
+    pool, scales = mla.new_pool(d, inp.num_pages, DEV)
+    mla.append_latent(d, t["c_kv"], t["k_pe"], t["positions"], t["seq_ids"], t["block_table"],
+                      pool, scales)
+    qn = t["q_nope"].reshape(B * ql, H, wl.d_nope).contiguous()
+    qp = t["q_pe"].reshape(B * ql, H, wl.d_rope).contiguous()
+    q_start = torch.tensor([0, ql, 2 * ql], dtype=torch.int32, device=DEV)
+    ws = torch.empty(mla.prefill_workspace_size(d, B, inp.max_pages), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B * ql, H, wl.d_v), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B * ql, H), dtype=torch.float32, device=DEV)
+
+    def call():
+        mla.prefill_paged(d, qn, qp, q_start, ql, pool, scales, t["block_table"], t["seq_lens"],
+                          t["w_uk"], t["w_uv"], ws, out, lse)
+
+    call()
+    torch.cuda.synchronize()
+    eager = (out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.zero_()
+        lse.zero_()
+        ws.zero_()                               # the workspace is rebuilt by every call
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager[0].view(torch.int16)), f"replay {i}: out"
+        assert torch.equal(lse, eager[1]), f"replay {i}: lse"
