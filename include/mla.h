@@ -155,7 +155,8 @@ mla_status_t mla_project_append(const mla_dims_t* dims, int32_t d_model, const v
  * per-head K_nope and V of every addressable token and the shared RoPE keys,
  * bf16: with P = round_up(max_pages * page_size, 32), two 256-byte aligned
  * blocks of B * n_heads * 128 * P * 2 bytes and one of B * 64 * P * 2 bytes.
- * Returns 0 for unsupported dims, B <= 0 or max_pages <= 0.
+ * Returns 0 for unsupported dims, B <= 0, max_pages <= 0 or
+ * max_pages * page_size > 2^24.
  */
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t B, int32_t max_pages);
 
@@ -186,13 +187,18 @@ size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t B, int32_t max
  *               mla_decode_paged (an fp8 cache is dequantised as code * scale
  *               rounded to bf16, as in decode)
  *   w_uk, w_uv  bf16 [H][d_c][d_nope] and [H][d_c][d_v]
- *   workspace   >= mla_prefill_workspace_size() bytes, 256-byte aligned
+ *   workspace   >= mla_prefill_workspace_size() bytes, 256-byte aligned (no
+ *               initialisation; every call rebuilds it)
  *   out         bf16 [T][H][d_v] (written): sum_t p_t V_h[t]
  *   lse         fp32 [T][H] natural-log normaliser of the scores, or NULL
  * with s_t = softmax_scale * (q_nope . K_h[t] + RoPE(q_pe) . k_rot[t]).
  * K and V are rounded to bf16 in the workspace, scores and the softmax are
  * fp32, P is rounded to bf16 for the P.V product.  Supported for d_c 512,
- * d_rope 64 and d_nope = d_v = 128 (else MLA_ERR_UNSUPPORTED).
+ * d_rope 64 and d_nope = d_v = 128, B <= 65535, max_q_len <= 2^24 and
+ * max_pages * page_size <= 2^24 (else MLA_ERR_UNSUPPORTED); MLA_ERR_WORKSPACE
+ * when ws_bytes is too small, MLA_ERR_INVALID_ARG for NULL or misaligned
+ * pointers (16 bytes for the bf16 arrays and the pool) or scales given for a
+ * bf16 cache / missing for an fp8 one, all before anything is enqueued.
  * Rows outside [0, T) are neither read nor written.  T == 0 or
  * max_q_len == 0 is a no-op.
  */
@@ -325,9 +331,10 @@ const char* mla_last_hip_error(void);
  * Kernel timing hooks for benchmarks (not part of the method).
  * mla_profile_begin(n) creates n pairs of HIP events; while active, each
  * mla_decode_paged, mla_decode_paged_multi and mla_prefill_paged call records
- * one pair around its main attention kernel on its stream.  mla_profile_end() waits for the recorded events, writes the
- * summed duration in milliseconds and the number of recorded launches, and
- * releases the events.  Not thread-safe; for single-threaded benchmarks only.
+ * one pair around its main attention kernel on its stream.
+ * mla_profile_end() waits for the recorded events, writes the summed
+ * duration in milliseconds and the number of recorded launches, and releases
+ * the events.  Not thread-safe; for single-threaded benchmarks only.
  */
 mla_status_t mla_profile_begin(int32_t max_records);
 mla_status_t mla_profile_end(double* total_ms, int32_t* n_records);
