@@ -343,31 +343,33 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
   const uint16_t* kn_b = a.kn + static_cast<int64_t>(b) * a.s_pad * a.H * kPfDh;
   const uint16_t* vt_bh = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * a.s_pad;
   // copies of key tile nt into slot base: 8 K_nope, 4 K_rope and 8 V^T copies
-  // of 1 KB, five per wave; lane l of a copy fills LDS bytes [16 l, +16)
+  // of 1 KB, five per wave; lane l of a copy fills LDS bytes [16 l, +16).
+  // Each lane's sources for tile 0 are formed once; tile nt adds a uniform
+  // offset (nt tiles of 32 tokens) to each of them
+  const uint16_t* src_kn[2];
+  const uint16_t* src_vt[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int k = wave + 4 * k2;
+    const int kr = 4 * k + (lane >> 4);
+    src_kn[k2] = kn_b + (static_cast<int64_t>(kr) * a.H + h) * kPfDh + 8 * ((lane & 15) ^ (kr & 15));
+    const int j = 16 * k + (lane >> 2);
+    src_vt[k2] = vt_bh + static_cast<int64_t>(j) * a.s_pad + 8 * ((lane & 3) ^ ((j >> 2) & 3));
+  }
+  const uint16_t* src_kr;
+  {
+    const int kr = 8 * wave + (lane >> 3);
+    src_kr = kr_b + kr * kPfDr + 8 * ((lane & 7) ^ (kr & 7));
+  }
   auto issue = [&](int nt, char* base) {
-    const int t0 = kPfKTile * nt;
+    const int64_t t0 = static_cast<int64_t>(kPfKTile) * nt;
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int k = wave + 4 * k2;
-      const int kr = 4 * k + (lane >> 4);
-      const int lc = (lane & 15) ^ (kr & 15);
-      lds_dma16_v(kn_b + (static_cast<int64_t>(t0 + kr) * a.H + h) * kPfDh + 8 * lc,
-                  lds_addr(base + kSlotKn + 1024 * k));
-    }
-    {
-      const int kr = 8 * wave + (lane >> 3);
-      const int lc = (lane & 7) ^ (kr & 7);
-      lds_dma16_v(kr_b + static_cast<int64_t>(t0 + kr) * kPfDr + 8 * lc,
-                  lds_addr(base + kSlotKr + 1024 * wave));
-    }
+    for (int k2 = 0; k2 < 2; ++k2)
+      lds_dma16_v(src_kn[k2] + t0 * a.H * kPfDh, lds_addr(base + kSlotKn + 1024 * (wave + 4 * k2)));
+    lds_dma16_v(src_kr + t0 * kPfDr, lds_addr(base + kSlotKr + 1024 * wave));
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int k = wave + 4 * k2;
-      const int j = 16 * k + (lane >> 2);
-      const int lc = (lane & 3) ^ ((j >> 2) & 3);
-      lds_dma16_v(vt_bh + static_cast<int64_t>(j) * a.s_pad + t0 + 8 * lc,
-                  lds_addr(base + kSlotVt + 1024 * k));
-    }
+    for (int k2 = 0; k2 < 2; ++k2)
+      lds_dma16_v(src_vt[k2] + t0, lds_addr(base + kSlotVt + 1024 * (wave + 4 * k2)));
   };
 
   float m = kNegInf, l = 0.f;
