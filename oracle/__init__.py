@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for MLA absorbed decode.
+"""fp64 CPU oracle for MLA absorbed decode, the latent down-projection and
+explicit-form prefill.
 
 TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's CPU
 baseline may import, call or execute anything under oracle/.  It shares no

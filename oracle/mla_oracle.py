@@ -1,4 +1,6 @@
-"""Plain, slow fp64 CPU oracle for Multi-head Latent Attention (MLA) decode.
+"""Plain, slow fp64 CPU oracle for Multi-head Latent Attention (MLA) decode
+(single and multi-token queries), the down-projection into the latent, and
+prefill in the explicit form.
 
 TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's CPU
 baseline may import, call or execute anything under oracle/.  It shares no
