@@ -15,20 +15,26 @@
 //   k_up       one workgroup of four waves per (head, 1024 tokens), launched
 //              once for K and once for V: the head's [512 x 128] weight sits
 //              in LDS and is read with the gfx950 transpose read; each wave
-//              computes 64 tokens x 128 columns, its latent rows going from
-//              the paged pool straight into MFMA registers, the next half of
-//              the reduction loading while this half's MFMAs run.  K_nope is written [t][h][128],
-//              V transposed [h][128][t] (the MFMA operands are swapped for V,
-//              so both stores are 64-byte runs).
+//              computes 64 tokens x 128 columns (two 32-token blocks sharing
+//              every weight operand), its latent rows going from the paged
+//              pool straight into MFMA registers in four quarters of the
+//              reduction, the next quarter loading while this quarter's
+//              MFMAs run; an fp8 cache's codes become bf16 (code * scale) at
+//              the MFMA.  K_nope is written [t][h][128], V transposed
+//              [h][128][t] (the MFMA operands are swapped for V, so both
+//              stores are 64-byte runs); the head-0 workgroups of the K launch
+//              also write the shared RoPE keys [t][64] as bf16.
 //   k_prefill  one workgroup of four waves per (sequence, head, 128 new
-//              tokens); each wave owns 32 queries.  Keys stream in 32-token
-//              tiles through a four-slot LDS ring filled by global->LDS
-//              copies three tiles ahead.  The score tile is computed transposed,
-//              S^T = K . Q^T (32x32x16 bf16 MFMA, Q in registers), so each
-//              lane holds 16 keys of one query: the online-softmax row max
-//              needs one cross-half exchange, and P^T goes straight from the
-//              accumulators into the B operand of O^T = V^T . P^T, whose
-//              accumulators keep the query on the lane as well.
+//              tokens); each wave owns 32 queries.  K_nope, RoPE-key and V^T
+//              tiles of 32 keys stream from the workspace through a four-slot
+//              LDS ring filled by global->LDS copies three tiles ahead.  The
+//              score tile is computed transposed, S^T = K . Q^T (32x32x16 bf16
+//              MFMA, Q in registers), so each lane holds 16 keys of one query:
+//              the online-softmax row max needs one cross-half exchange, and
+//              P^T goes straight from the accumulators into the B operand of
+//              O^T = V^T . P^T, whose accumulators keep the query on the lane
+//              as well.  The softmax offset moves only when a row max rises by
+//              more than 8 (base 2), so rescaling O is rare.
 //   Workgroups of one (sequence, head) sit on one XCD (blockIdx mod 8), so
 //   their K/V tiles are shared through that XCD's L2; the query tiles that
 //   see the most keys start first.
