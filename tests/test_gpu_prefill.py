@@ -141,3 +141,23 @@ def test_full_size_sampled():
     print("[prefill] full size B=2 S=8192 chunk=4096 H=128", flush=True)
     out, lse, starts, _ = run_prefill(inp, d)
     compare(inp, out, lse, starts, heads=[0, 77, 127], rows=[0, 1, 127, 128, 2047, 4095])
+
+
+def test_rows_before_the_buffer_are_skipped():
+    # q_start[0] = -5: the chunk's first five rows lie outside [0, T) and are
+    # neither read nor written; the other rows keep their positions
+    wl = _wl("v3_h2_c25", 2, (70,), 25)
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    qn = t["q_nope"].reshape(25, 2, 128)[5:].contiguous()
+    qp = t["q_pe"].reshape(25, 2, 64)[5:].contiguous()
+    q_start = torch.tensor([-5, 20], dtype=torch.int32, device="cuda")
+    out = torch.full((20, 2, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((20, 2), 3.0, dtype=torch.float32, device="cuda")
+    mla.prefill_paged(d, qn, qp, q_start, 25, pool, scales, t["block_table"], t["seq_lens"],
+                      t["w_uk"], t["w_uv"], out=out, lse=lse)
+    torch.cuda.synchronize()
+    ref = reference_prefill(inp, rows=list(range(5, 25)))
+    assert_close(out.float().cpu().numpy().astype(np.float64), ref["out"][0], "out")
+    assert np.max(np.abs(lse.cpu().numpy() - ref["lse"][0])) <= 1e-2
