@@ -71,6 +71,18 @@ __device__ __forceinline__ int vt_slot(int k) {
   return 8 * (2 * s + g) + 4 * e + i;
 }
 
+// Lanes 2m (even) and 2m + 1 (odd) each hold values x0, x1 of two adjacent
+// rows (index i, i + 1) in their own column.  Returns, as two bf16 in one
+// word, the even lane's row i of both columns (its own x0, the odd lane's x0)
+// and the odd lane's row i + 1 of both columns (the even lane's x1, its own
+// x1): the odd lane hands over x0, the even lane x1, by one DPP swap.
+__device__ __forceinline__ uint32_t pair_transpose(float x0, float x1, int odd) {
+  const float send = odd ? x0 : x1;
+  const float recv = __int_as_float(__builtin_amdgcn_update_dpp(
+      0, __float_as_int(send), 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, false));
+  return odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
+}
+
 // ---------------------------------------------------------------------------
 // Up-projection
 // ---------------------------------------------------------------------------
@@ -221,13 +233,17 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
         // at the stores in scalar registers, not hoisted out of the loop)
         int64_t ts = static_cast<int64_t>(a.H) * kPfDh;                // token stride
         __asm__ volatile("" : "+s"(ts));
+        // lanes 2m and 2m + 1 swap one value (a 2 x 2 transpose), so each
+        // stores two adjacent columns of one token as one 4-byte word: the
+        // even lane token 8 (i/4) + i%4, the odd lane the next token
         uint16_t* kb = a.kn + ((static_cast<int64_t>(b) * a.s_pad + tblk) * a.H + h) * kPfDh +
-                       4 * half * ts + r;
+                       4 * half * ts + (r & ~1);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            kb[(8 * (i >> 2) + (i & 3)) * ts + 32 * ct] = f32_to_bf16_bits(acc[rb][ct][i]);
+          for (int i = 0; i < 16; i += 2)
+            *reinterpret_cast<uint32_t*>(kb + (8 * (i >> 2) + (i & 3) + (r & 1)) * ts + 32 * ct) =
+                pair_transpose(acc[rb][ct][i], acc[rb][ct][i + 1], r & 1);
       } else {
         // acc[rb][ct][i]: column 32 ct + 8 (i/4) + 4 half + i%4, token tblk + r,
         // stored at slot vt_slot(r) of its 32-token block; the lane's part of
@@ -236,13 +252,17 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
         // at the stores in scalar registers, not hoisted out of the loop)
         int64_t cs = a.s_pad;                                           // column stride
         __asm__ volatile("" : "+s"(cs));
+        // lanes 2m and 2m + 1 hold adjacent slots; after the 2 x 2 transpose
+        // each stores both slots of one column as one 4-byte word: the even
+        // lane column 32 ct + 8 (i/4) + 4 half + i%4, the odd lane the next
         uint16_t* vb = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * cs + tblk +
-                       4 * half * cs + vt_slot(r);
+                       4 * half * cs + vt_slot(r & ~1);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            vb[(32 * ct + 8 * (i >> 2) + (i & 3)) * cs] = f32_to_bf16_bits(acc[rb][ct][i]);
+          for (int i = 0; i < 16; i += 2)
+            *reinterpret_cast<uint32_t*>(vb + (32 * ct + 8 * (i >> 2) + (i & 3) + (r & 1)) * cs) =
+                pair_transpose(acc[rb][ct][i], acc[rb][ct][i + 1], r & 1);
       }
     }
   }
