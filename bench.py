@@ -189,21 +189,20 @@ def bench_prefill(args):
     ws = torch.empty(mla.prefill_workspace_size(d, B, inp.max_pages), dtype=torch.uint8, device=dev)
     out = torch.empty((B * n, H, wl.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B * n, H), dtype=torch.float32, device=dev)
-    call = lambda: mla.prefill_paged(d, qn, qp, q_start, n, pool, None, t["block_table"],
-                                     t["seq_lens"], t["w_uk"], t["w_uv"], ws, out, lse)
+    call = lambda ev=None: mla.prefill_paged(d, qn, qp, q_start, n, pool, None, t["block_table"],
+                                             t["seq_lens"], t["w_uk"], t["w_uv"], ws, out, lse, events=ev)
     for _ in range(args.warmup):
         call()
+    evs = kernel_events(torch, args.steps)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    mla.profile_begin(args.steps)
     e0.record()
-    for _ in range(args.steps):
-        call()
+    for i in range(args.steps):
+        call(evs[i])
     e1.record()
     torch.cuda.synchronize()
-    attn_ms, n_rec = mla.profile_end()
     ms = e0.elapsed_time(e1) / args.steps
-    attn_us = attn_ms / max(1, n_rec) * 1e3
+    attn_us = mean_event_ms(evs) * 1e3
     # new token i sits at position S - n + i and sees S - n + i + 1 keys
     keys = n * (S - n) + n * (n + 1) // 2
     attn_flops = 2.0 * B * H * keys * (wl.d_nope + wl.d_rope + wl.d_v)
@@ -231,6 +230,21 @@ def bench_prefill(args):
     if args.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline_prefill(inp)
     print(json.dumps(line), flush=True)
+
+
+def kernel_events(torch, n: int):
+    """n (start, stop) event pairs for the library's timed entry points, each
+    event created (by one record) before the timed region starts."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    return evs
+
+
+def mean_event_ms(evs) -> float:
+    """Mean milliseconds between the events of each pair (after a synchronise)."""
+    return sum(a.elapsed_time(b) for a, b in evs) / max(1, len(evs))
 
 
 def cpu_baseline_prefill(inp):
@@ -380,33 +394,34 @@ def main():
     q_pe = t["q_pe"].reshape(BQ, H, wl.d_rope)
     q_pos = t["q_pos"].reshape(BQ).contiguous()
 
+    # ev: (start, stop) events recorded around the split kernel on the stream
     if ql == 1:
-        def decode():
+        def decode(ev=None):
             mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], args.num_splits,
-                             ws, o_lat, lse)
+                             ws, o_lat, lse, events=ev)
     else:
-        def decode():
+        def decode(ev=None):
             mla.decode_paged_multi(d, q.view(B, ql, H, R), pool, scales, t["block_table"],
                                    t["seq_lens"], args.num_splits, ws, o_lat.view(B, ql, H, wl.d_c),
-                                   lse.view(B, ql, H))
+                                   lse.view(B, ql, H), events=ev)
 
-    def step():
+    def step(ev=None):
         mla.append_latent(d, new_c, new_k, new_pos, new_sid, t["block_table"], pool, scales)
         mla.absorb_q(d, q_nope, q_pe, q_pos, t["w_uk"], q)
-        decode()
+        decode(ev)
         mla.out_proj(d, o_lat, t["w_uv"], out)
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    mla.profile_begin(args.steps)
+    evs = kernel_events(torch, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    split_ms_total, n_rec = mla.profile_end()
+    split_ms = mean_event_ms(evs)
+    n_rec = len(evs)
     assert torch.isfinite(out.float()).all(), "non-finite output"
     eager_elapsed = elapsed
     if args.graph:
@@ -444,7 +459,6 @@ def main():
     attended = int(np.sum(np.maximum(0, inp.seq_lens[:, None].astype(np.int64) - ql + 1
                                      + np.arange(ql)[None, :])))
     flops = 2.0 * attended * H * (R + wl.d_c)
-    split_ms = split_ms_total / max(1, n_rec)
     achieved_gbs = split_bytes / (split_ms * 1e-3) / 1e9
     tflops = flops / (split_ms * 1e-3) / 1e12
     # the binding roof: HBM time of the bytes vs bf16 MFMA time of the flops

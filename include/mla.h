@@ -258,7 +258,10 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t B, int32_t num_
  * Results differ between split counts only by floating-point rounding.
  * fp8 cache (d_c = 512, d_rope = 64 only, else MLA_ERR_UNSUPPORTED): row_t is
  * the dequantised row code * scale[t] (zskr.cn section 5, mixed-precision
- * FP8 cache; fsdata.site section 3.1), rounded to bf16 before the products.
+ * FP8 cache; fsdata.site section 3.1).  The codes enter the products exactly
+ * (every e4m3 value is a bf16 value) and the token's scale multiplies its
+ * score q . code_t and its softmax weight (p_t * scale[t], rounded to bf16 for
+ * the P . V product).
  */
 mla_status_t mla_decode_paged(const mla_dims_t* dims, const void* q, const void* pool,
                               const float* scales, const int32_t* block_table, int32_t max_pages,
@@ -328,16 +331,27 @@ const char* mla_status_string(mla_status_t status);
 const char* mla_last_hip_error(void);
 
 /*
- * Kernel timing hooks for benchmarks (not part of the method).
- * mla_profile_begin(n) creates n pairs of HIP events; while active, each
- * mla_decode_paged, mla_decode_paged_multi and mla_prefill_paged call records
- * one pair around its main attention kernel on its stream.
- * mla_profile_end() waits for the recorded events, writes the summed
- * duration in milliseconds and the number of recorded launches, and releases
- * the events.  Not thread-safe; for single-threaded benchmarks only.
+ * mla_decode_paged_timed, mla_prefill_paged_timed - mla_decode_paged_multi and
+ * mla_prefill_paged with two caller-owned HIP events (hipEvent_t values
+ * created by the caller, or NULL) recorded on `stream` immediately before and
+ * after the call's main kernel: the split attention of decode, the attention
+ * kernel of prefill.  For measurements; arguments, errors and results are
+ * otherwise those of the plain calls, and nothing is kept between calls.  A
+ * failing event record returns MLA_ERR_HIP.
  */
-mla_status_t mla_profile_begin(int32_t max_records);
-mla_status_t mla_profile_end(double* total_ms, int32_t* n_records);
+mla_status_t mla_decode_paged_timed(const mla_dims_t* dims, const void* q, const void* pool,
+                                    const float* scales, const int32_t* block_table,
+                                    int32_t max_pages, int32_t num_pages, const int32_t* seq_lens,
+                                    int32_t B, int32_t q_len, int32_t num_splits, void* workspace,
+                                    size_t ws_bytes, void* o_lat, float* lse, void* ev_start,
+                                    void* ev_stop, void* stream);
+mla_status_t mla_prefill_paged_timed(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
+                                     const int32_t* q_start, int32_t T, int32_t max_q_len,
+                                     const void* pool, const float* scales, const int32_t* block_table,
+                                     int32_t max_pages, int32_t num_pages, const int32_t* seq_lens,
+                                     int32_t B, const void* w_uk, const void* w_uv, void* workspace,
+                                     size_t ws_bytes, void* out, float* lse, void* ev_start,
+                                     void* ev_stop, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,7 @@ _API = (
     "decode_paged", "decode_paged_multi", "decode_workspace_size", "make_dims", "new_pool",
     "new_workspace", "out_proj", "prefill_paged", "prefill_workspace_size", "project_append",
     "project_append_workspace_size",
-    "pool_shape", "profile_begin", "profile_end", "status_string",
+    "pool_shape", "status_string",
 )
 __all__ = list(_API)
 

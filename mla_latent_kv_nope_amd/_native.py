@@ -47,7 +47,7 @@ EXPORTS = (
     "mla_append_latent", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_paged",
     "mla_decode_paged_multi", "mla_project_append", "mla_project_append_workspace_size",
     "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_last_hip_error",
-    "mla_profile_begin", "mla_profile_end", "mla_prefill_workspace_size", "mla_prefill_paged",
+    "mla_decode_paged_timed", "mla_prefill_paged_timed", "mla_prefill_workspace_size", "mla_prefill_paged",
 )
 
 _P = ctypes.c_void_p
@@ -92,10 +92,12 @@ def _load() -> ctypes.CDLL:
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_hip_error.argtypes = []
     lib.mla_last_hip_error.restype = ctypes.c_char_p
-    lib.mla_profile_begin.argtypes = [_I]
-    lib.mla_profile_begin.restype = ctypes.c_int
-    lib.mla_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I)]
-    lib.mla_profile_end.restype = ctypes.c_int
+    lib.mla_decode_paged_timed.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P,
+                                           ctypes.c_size_t, _P, _P, _P, _P, _P]
+    lib.mla_decode_paged_timed.restype = ctypes.c_int
+    lib.mla_prefill_paged_timed.argtypes = [_DP, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, _P,
+                                            _P, ctypes.c_size_t, _P, _P, _P, _P, _P]
+    lib.mla_prefill_paged_timed.restype = ctypes.c_int
     return lib
 
 

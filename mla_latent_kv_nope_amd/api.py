@@ -53,6 +53,23 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _event_handles(events) -> Tuple[Optional[int], Optional[int]]:
+    """(start, stop) torch.cuda.Event pair -> raw hipEvent_t handles.  A torch
+    event creates its HIP event at its first record, so an uncreated one is
+    recorded once here first; the library then records it again on the call's
+    stream around the main kernel."""
+    if events is None:
+        return None, None
+    out = []
+    for ev in events:
+        if not isinstance(ev, torch.cuda.Event):
+            raise TypeError("events must be a pair of torch.cuda.Event")
+        if not ev.cuda_event:
+            ev.record()
+        out.append(ev.cuda_event)
+    return out[0], out[1]
+
+
 def _req(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Optional[tuple] = None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -177,7 +194,9 @@ def new_workspace(d: Dims, B: int, num_splits: int = 0, device="cuda") -> torch.
 def decode_paged(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Optional[torch.Tensor],
                  block_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int = 0,
                  workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
-                 lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+                 lse: Optional[torch.Tensor] = None, want_lse: bool = True, events=None):
+    """mla_decode_paged; with `events` = (start, stop) torch.cuda.Event, the call
+    goes through mla_decode_paged_timed and the events bracket the split kernel."""
     B = q.shape[0]
     H, R = d.n_heads, d.d_c + d.d_rope
     _req(q, "q", torch.bfloat16, (B, H, R))
@@ -201,17 +220,25 @@ def decode_paged(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Optional[
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if lse is not None:
         _req(lse, "lse", torch.float32, (B, H))
-    st = lib.mla_decode_paged(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales), _ptr(block_table),
-                              block_table.shape[1], num_pages, _ptr(seq_lens), B, int(num_splits),
-                              _ptr(workspace), workspace.numel(), _ptr(o_lat), _ptr(lse), _stream())
-    _check("mla_decode_paged", st)
+    if events is None:
+        st = lib.mla_decode_paged(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales), _ptr(block_table),
+                                  block_table.shape[1], num_pages, _ptr(seq_lens), B, int(num_splits),
+                                  _ptr(workspace), workspace.numel(), _ptr(o_lat), _ptr(lse), _stream())
+        _check("mla_decode_paged", st)
+    else:
+        e0, e1 = _event_handles(events)
+        st = lib.mla_decode_paged_timed(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales),
+                                        _ptr(block_table), block_table.shape[1], num_pages,
+                                        _ptr(seq_lens), B, 1, int(num_splits), _ptr(workspace),
+                                        workspace.numel(), _ptr(o_lat), _ptr(lse), e0, e1, _stream())
+        _check("mla_decode_paged_timed", st)
     return o_lat, lse
 
 
 def decode_paged_multi(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Optional[torch.Tensor],
                        block_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int = 0,
                        workspace: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+                       lse: Optional[torch.Tensor] = None, want_lse: bool = True, events=None):
     """mla_decode_paged_multi: q is [B][q_len][H][R]; returns o_lat [B][q_len][H][d_c]
     and lse [B][q_len][H] (or None)."""
     if q.dim() != 4:
@@ -239,11 +266,19 @@ def decode_paged_multi(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Opt
         lse = torch.empty((B, q_len, H), dtype=torch.float32, device=q.device)
     if lse is not None:
         _req(lse, "lse", torch.float32, (B, q_len, H))
-    st = lib.mla_decode_paged_multi(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales),
-                                    _ptr(block_table), block_table.shape[1], num_pages,
-                                    _ptr(seq_lens), B, int(q_len), int(num_splits), _ptr(workspace),
-                                    workspace.numel(), _ptr(o_lat), _ptr(lse), _stream())
-    _check("mla_decode_paged_multi", st)
+    if events is None:
+        st = lib.mla_decode_paged_multi(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales),
+                                        _ptr(block_table), block_table.shape[1], num_pages,
+                                        _ptr(seq_lens), B, int(q_len), int(num_splits), _ptr(workspace),
+                                        workspace.numel(), _ptr(o_lat), _ptr(lse), _stream())
+        _check("mla_decode_paged_multi", st)
+    else:
+        e0, e1 = _event_handles(events)
+        st = lib.mla_decode_paged_timed(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales),
+                                        _ptr(block_table), block_table.shape[1], num_pages,
+                                        _ptr(seq_lens), B, int(q_len), int(num_splits), _ptr(workspace),
+                                        workspace.numel(), _ptr(o_lat), _ptr(lse), e0, e1, _stream())
+        _check("mla_decode_paged_timed", st)
     return o_lat, lse
 
 
@@ -265,17 +300,6 @@ def cache_bytes_per_token(d: Dims) -> int:
     return int(lib.mla_cache_bytes_per_token(ctypes.byref(d)))
 
 
-def profile_begin(max_records: int) -> None:
-    _check("mla_profile_begin", lib.mla_profile_begin(int(max_records)))
-
-
-def profile_end() -> Tuple[float, int]:
-    ms = ctypes.c_double(0.0)
-    n = ctypes.c_int32(0)
-    _check("mla_profile_end", lib.mla_profile_end(ctypes.byref(ms), ctypes.byref(n)))
-    return ms.value, n.value
-
-
 def prefill_workspace_size(d: Dims, B: int, max_pages: int) -> int:
     return int(lib.mla_prefill_workspace_size(ctypes.byref(d), int(B), int(max_pages)))
 
@@ -285,7 +309,7 @@ def prefill_paged(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_start: to
                   block_table: torch.Tensor, seq_lens: torch.Tensor, w_uk: torch.Tensor,
                   w_uv: torch.Tensor, workspace: Optional[torch.Tensor] = None,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                  want_lse: bool = True):
+                  want_lse: bool = True, events=None):
     """mla_prefill_paged: q_nope [T][H][d_nope], q_pe [T][H][d_rope], q_start [B+1]
     (device int32); returns out [T][H][d_v] and lse [T][H] (or None)."""
     H = d.n_heads
@@ -320,10 +344,12 @@ def prefill_paged(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_start: to
         lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
     if lse is not None:
         _req(lse, "lse", torch.float32, (T, H))
-    st = lib.mla_prefill_paged(ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(q_start), T,
-                               int(max_q_len), _ptr(pool), _ptr(scales), _ptr(block_table),
-                               max_pages, num_pages,
-                               _ptr(seq_lens), B, _ptr(w_uk), _ptr(w_uv), _ptr(workspace),
-                               workspace.numel(), _ptr(out), _ptr(lse), _stream())
-    _check("mla_prefill_paged", st)
+    args = (ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(q_start), T, int(max_q_len), _ptr(pool),
+            _ptr(scales), _ptr(block_table), max_pages, num_pages, _ptr(seq_lens), B, _ptr(w_uk),
+            _ptr(w_uv), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse))
+    if events is None:
+        _check("mla_prefill_paged", lib.mla_prefill_paged(*args, _stream()))
+    else:
+        e0, e1 = _event_handles(events)
+        _check("mla_prefill_paged_timed", lib.mla_prefill_paged_timed(*args, e0, e1, _stream()))
     return out, lse

@@ -42,6 +42,7 @@
 //        chains), and accumulate O for 2 column blocks; waves 4-7 accumulate
 //        O for 6 column blocks each and issue all tile copies, so the
 //        copies' issue stalls never hold up the scoring waves.
+#include <atomic>
 #include <type_traits>
 
 #include "mla_common.hpp"
@@ -56,33 +57,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // offset by more than that; such a piece is recomputed with its true maximum.
 constexpr float kHeadroom = 64.0f;  // log2 units
 
-// MFMA operand reads kept in flight ahead of their MFMA (QK^T, PV)
-#ifndef MLA_QK_AHEAD
-#define MLA_QK_AHEAD 4
-#endif
-#ifndef MLA_PV_AHEAD
-#define MLA_PV_AHEAD 3
-#endif
-#ifndef MLA_LOADER_WAVES
-#define MLA_LOADER_WAVES 0
-#endif
-constexpr int kQkAhead = MLA_QK_AHEAD;
-constexpr int kPvAhead = MLA_PV_AHEAD;
-// specialised path: K operand reads in flight ahead of their MFMA pairs, and
-// whether the loader waves issue a tile's copies after their PV instead of
-// right after the barrier
-#ifndef MLA_QK2_AHEAD
-#define MLA_QK2_AHEAD 2
-#endif
-#ifndef MLA_SPEC_LATE_ISSUE
-#define MLA_SPEC_LATE_ISSUE 0
-#endif
-constexpr int kQk2Ahead = MLA_QK2_AHEAD;
-constexpr bool kSpecLateIssue = MLA_SPEC_LATE_ISSUE != 0;
-#ifndef MLA_SPEC_QK_PRIO
-#define MLA_SPEC_QK_PRIO 0
-#endif
-constexpr int kSpecQkPrio = MLA_SPEC_QK_PRIO;   // issue priority of the QK waves
+// MFMA operand reads kept in flight ahead of their MFMA: QK^T of the general
+// layout, and the specialised layout's K reads (each feeding two MFMAs)
+constexpr int kQkAhead = 4;
+constexpr int kQk2Ahead = 2;
 
 template <int DC, int DR, int NW, bool FP8 = false>
 struct DecodeCfg {
@@ -103,8 +81,7 @@ struct DecodeCfg {
   // score 32 heads each, waves 4-7 accumulate most of O and issue every tile
   // copy (loader i copies the tile's 8-row group i).
   static constexpr bool SPEC = NW == 8 && DC == 512 && DR == 64 && !FP8;
-  static constexpr int LW = SPEC ? 4
-                            : (MLA_LOADER_WAVES > 0 && MLA_LOADER_WAVES < NW) ? MLA_LOADER_WAVES : NW;
+  static constexpr int LW = SPEC ? 4 : NW;
   static constexpr int LD_HI = (INSTR + LW - 1) / LW;  // loads of loaders < INSTR % LW (or all)
   static constexpr int LD_LO = INSTR / LW;
   static constexpr int K32 = R / 32;                 // full 32-wide QK chunks
@@ -203,11 +180,14 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   static_assert(!Cfg::BLOCKED || CPW % 4 == 0, "blocked PV reads start at a multiple of 4 column blocks");
   // tile ring, (fp8: staging slots,) then two P slots (the second also
   // carries the per-head 1/l at the end of a piece; the first the overflow vote)
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES + Cfg::STAGE_BYTES + 2 * PSLOT];
+  // (fp8: then the per-token scales of the two bf16 tiles in use)
+  constexpr int SCL_BYTES = FP8 ? 2 * kTile * 4 : 0;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES + Cfg::STAGE_BYTES + 2 * PSLOT + SCL_BYTES];
   char* const stage = lds + Cfg::NBUF * Cfg::TILE_BYTES;
   char* const pbuf = stage + Cfg::STAGE_BYTES;
   int* const vote = reinterpret_cast<int*>(pbuf);
   float* const inv_share = reinterpret_cast<float*>(pbuf + PSLOT);
+  float* const scl = reinterpret_cast<float*>(pbuf + 2 * PSLOT);
 
   // Piece index of this workgroup.  Workgroups are dispatched round-robin
   // over the 8 XCDs (blockIdx % 8); consecutive pieces, which are mostly the
@@ -543,11 +523,13 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       for (int u = threadIdx.x; u < kTile * UPR; u += Cfg::THREADS) {
         const int r = u / UPR, c = u - r * UPR;
         const uint2 x = *reinterpret_cast<const uint2*>(src + r * R + 8 * c);
-        const float scl = tok0 + r < S ? sls[r] : sls[0];
-        const uint4 y = {fp8x2_to_bf16x2<false>(x.x, scl), fp8x2_to_bf16x2<true>(x.x, scl),
-                         fp8x2_to_bf16x2<false>(x.y, scl), fp8x2_to_bf16x2<true>(x.y, scl)};
+        const uint4 y = {fp8x2_to_bf16x2<false>(x.x), fp8x2_to_bf16x2<true>(x.x),
+                         fp8x2_to_bf16x2<false>(x.y), fp8x2_to_bf16x2<true>(x.y)};
         *reinterpret_cast<uint4*>(dst + lds_off<Cfg>(r, c)) = y;
       }
+      // the tile's per-token scales, applied to its scores and to P (rows
+      // past the sequence, masked, take row 0's finite scale)
+      if (threadIdx.x < kTile) scl[bslot * kTile + threadIdx.x] = tok0 + threadIdx.x < S ? sls[threadIdx.x] : sls[0];
     };
 
     if constexpr (Cfg::SPEC) {
@@ -669,7 +651,6 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     };
 
     if (qkw) {
-      if constexpr (kSpecQkPrio > 0) __builtin_amdgcn_s_setprio(kSpecQkPrio);
       const int hq = QH * wave;                   // first head of this wave
       // Q of two 16-head groups g: lane holds head hq + 16g + l16, elements
       // [32kc + 8quad, +8) of chunk kc
@@ -818,9 +799,8 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         if (AHEAD < ntiles) issue_tile(lt0 + AHEAD, AHEAD % Cfg::NBUF);
         for (int it = 1; it < ntiles; ++it) {
           sync_tile(it);
-          if (!kSpecLateIssue && it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
+          if (it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
           pv_cols(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (it - 1) & 1, cbf, oo);
-          if (kSpecLateIssue && it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
         }
         block_barrier();
         pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1, cbf, oo);
@@ -923,14 +903,33 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // ---- online softmax of one tile; sacc[tb][i] is token 16tb + 4*quad + i,
     // head l16.  Returns P as the PV A operand: k slot 8*quad + j <-> token
     // (j < 4 ? 4quad + j : 16 + 4quad + j - 4).
-    auto softmax = [&](const f32x4* sacc, int tok0, bool set_offset) -> bf16x8 {
+    // fp8 cache: the tile holds the exact codes; the score of token t is
+    // scale_t * (q . code_t) and P carries scale_t into the P . V product
+    // (the tile's scales sit in scl[slot]).
+    auto softmax = [&](const f32x4* sacc, int tok0, bool set_offset, int slot) -> bf16x8 {
+      float sc[8];
+      if constexpr (FP8) {
+        const float* sp = scl + slot * kTile + 4 * quad;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[i] = lo[i];
+          sc[4 + i] = hi[i];
+        }
+      }
+      auto xval = [&](int tbk, int i) -> float {
+        const float v = sacc[tbk][i];
+        if constexpr (FP8) return v * sc[4 * tbk + i];
+        return v;
+      };
       float x[8];
       float mt;
       if (tok0 + kTile <= S) {                    // whole tile valid: no mask
 #pragma unroll
         for (int tbk = 0; tbk < 2; ++tbk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[4 * tbk + i] = sacc[tbk][i];
+          for (int i = 0; i < 4; ++i) x[4 * tbk + i] = xval(tbk, i);
         mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                    fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       } else {
@@ -940,7 +939,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * tbk + 4 * quad + i;
-            const float v = (tok0 + t < S) ? sacc[tbk][i] : -INFINITY;
+            const float v = (tok0 + t < S) ? xval(tbk, i) : -INFINITY;
             x[4 * tbk + i] = v;
             mt = fmaxf(mt, v);
           }
@@ -959,7 +958,8 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j], a.scale_log2, -m_use));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j + 1], a.scale_log2, -m_use));
         l_part += p0 + p1;
-        pu[j] = pack_bf16x2(p0, p1);
+        if constexpr (FP8) pu[j] = pack_bf16x2(p0 * sc[2 * j], p1 * sc[2 * j + 1]);
+        else pu[j] = pack_bf16x2(p0, p1);
       }
       return __builtin_bit_cast(bf16x8, pu);
     };
@@ -1034,7 +1034,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       if (qk_wave) {
         f32x4 sacc[2];
         qk(tb, sacc);
-        p_store(pslot, softmax(sacc, tok0, set_offset));
+        p_store(pslot, softmax(sacc, tok0, set_offset, pslot));
       }
     };
 
@@ -1311,19 +1311,23 @@ bool decode_supported(int d_c, int d_rope, int H, bool fp8) {
   return false;
 }
 
+// One piece per compute unit of the current device.  The count is cached per
+// device in atomics (a racing first query stores the same value).
 int decode_auto_parts(int B, int H) {
   (void)B;
   (void)H;
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return cus;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < kMaxDevices) cus[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {

@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
   auto row_ptr = [&](int64_t prow) { return pool + (prow * kPfRow + 8 * half) * ES; };
   auto to_bf16 = [&](const Raw& v, float sc) -> bf16x8 {
     if constexpr (FP8) {
-      return __builtin_bit_cast(bf16x8, make_uint4(fp8x2_to_bf16x2<false>(v.x, sc), fp8x2_to_bf16x2<true>(v.x, sc),
-                                                   fp8x2_to_bf16x2<false>(v.y, sc), fp8x2_to_bf16x2<true>(v.y, sc)));
+      return __builtin_bit_cast(bf16x8, make_uint4(fp8x2_to_bf16x2_scaled<false>(v.x, sc), fp8x2_to_bf16x2_scaled<true>(v.x, sc),
+                                                   fp8x2_to_bf16x2_scaled<false>(v.y, sc), fp8x2_to_bf16x2_scaled<true>(v.y, sc)));
     } else {
       (void)sc;
       return v;
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
             const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-              dst[k] = make_uint4(fp8x2_to_bf16x2<false>(w[2 * k], f), fp8x2_to_bf16x2<true>(w[2 * k], f),
-                                  fp8x2_to_bf16x2<false>(w[2 * k + 1], f), fp8x2_to_bf16x2<true>(w[2 * k + 1], f));
+              dst[k] = make_uint4(fp8x2_to_bf16x2_scaled<false>(w[2 * k], f), fp8x2_to_bf16x2_scaled<true>(w[2 * k], f),
+                                  fp8x2_to_bf16x2_scaled<false>(w[2 * k + 1], f), fp8x2_to_bf16x2_scaled<true>(w[2 * k + 1], f));
           } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) dst[k] = reinterpret_cast<const uint4*>(src)[k];

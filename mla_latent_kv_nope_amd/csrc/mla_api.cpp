@@ -1,13 +1,11 @@
 // C ABI of libmla (declared in include/mla.h): argument validation, workspace
-// layout, dispatch to the kernels, status codes, and the optional kernel
-// timing hooks.  Every check here runs before any HIP call, so invalid host
-// arguments enqueue nothing.
+// layout, dispatch to the kernels and status codes.  Every check here runs
+// before any HIP call, so invalid host arguments enqueue nothing.
 #include "../../include/mla.h"
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <vector>
 
 #include "mla_internal.hpp"
 #include "prefill.hpp"
@@ -50,13 +48,6 @@ mla_status_t from_hip(hipError_t e) {
   g_last_hip_error = hipGetErrorString(e);
   return MLA_ERR_HIP;
 }
-
-struct Profiler {
-  bool active = false;
-  std::vector<hipEvent_t> ev;  // [2 * max_records]: start, stop pairs
-  int used = 0;
-};
-Profiler g_prof;
 
 int effective_parts(int32_t num_splits, int B, int H) {
   return num_splits > 0 ? num_splits : mla::decode_auto_parts(B, H);
@@ -231,7 +222,8 @@ namespace {
 mla_status_t decode_impl(const mla_dims_t* d, const void* q, const void* pool, const float* scales,
                          const int32_t* block_table, int32_t max_pages, int32_t num_pages,
                          const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t num_splits,
-                         void* workspace, size_t ws_bytes, void* o_lat, float* lse, void* stream) {
+                         void* workspace, size_t ws_bytes, void* o_lat, float* lse, hipEvent_t e0,
+                         hipEvent_t e1, void* stream) {
   const mla_status_t st = check_dims(d);
   if (st != MLA_OK) return st;
   if (B <= 0 || max_pages <= 0 || num_pages <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
@@ -273,12 +265,6 @@ mla_status_t decode_impl(const mla_dims_t* d, const void* q, const void* pool, c
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse_off);
   a.o_lat = static_cast<uint16_t*>(o_lat);
   a.lse = lse;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (g_prof.active && 2 * g_prof.used + 1 < static_cast<int>(g_prof.ev.size())) {
-    e0 = g_prof.ev[2 * g_prof.used];
-    e1 = g_prof.ev[2 * g_prof.used + 1];
-    ++g_prof.used;
-  }
   return from_hip(mla::launch_decode(a, static_cast<hipStream_t>(stream), e0, e1));
 }
 
@@ -290,7 +276,7 @@ mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* po
                               int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
                               float* lse, void* stream) {
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, 1, num_splits,
-                     workspace, ws_bytes, o_lat, lse, stream);
+                     workspace, ws_bytes, o_lat, lse, nullptr, nullptr, stream);
 }
 
 mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const void* pool,
@@ -299,7 +285,17 @@ mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const vo
                                     int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
                                     float* lse, void* stream) {
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
-                     num_splits, workspace, ws_bytes, o_lat, lse, stream);
+                     num_splits, workspace, ws_bytes, o_lat, lse, nullptr, nullptr, stream);
+}
+
+mla_status_t mla_decode_paged_timed(const mla_dims_t* d, const void* q, const void* pool,
+                                    const float* scales, const int32_t* block_table, int32_t max_pages,
+                                    int32_t num_pages, const int32_t* seq_lens, int32_t B, int32_t q_len,
+                                    int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
+                                    float* lse, void* ev_start, void* ev_stop, void* stream) {
+  return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
+                     num_splits, workspace, ws_bytes, o_lat, lse, static_cast<hipEvent_t>(ev_start),
+                     static_cast<hipEvent_t>(ev_stop), stream);
 }
 
 size_t mla_prefill_workspace_size(const mla_dims_t* d, int32_t B, int32_t max_pages) {
@@ -310,13 +306,16 @@ size_t mla_prefill_workspace_size(const mla_dims_t* d, int32_t B, int32_t max_pa
   return mla::prefill_workspace_bytes(B, d->n_heads, s_cap);
 }
 
-mla_status_t mla_prefill_paged(const mla_dims_t* d, const void* q_nope, const void* q_pe,
-                               const int32_t* q_start, int32_t T, int32_t max_q_len,
-                               const void* pool, const float* scales, const int32_t* block_table,
-                               int32_t max_pages,
-                               int32_t num_pages, const int32_t* seq_lens, int32_t B,
-                               const void* w_uk, const void* w_uv, void* workspace,
-                               size_t ws_bytes, void* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mla_status_t prefill_impl(const mla_dims_t* d, const void* q_nope, const void* q_pe, const int32_t* q_start,
+                          int32_t T, int32_t max_q_len, const void* pool, const float* scales,
+                          const int32_t* block_table, int32_t max_pages, int32_t num_pages,
+                          const int32_t* seq_lens, int32_t B, const void* w_uk, const void* w_uv,
+                          void* workspace, size_t ws_bytes, void* out, float* lse, hipEvent_t e0,
+                          hipEvent_t e1, void* stream) {
   const mla_status_t st = check_dims(d);
   if (st != MLA_OK) return st;
   if (T < 0 || max_q_len < 0 || B <= 0 || max_pages <= 0 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
@@ -371,14 +370,35 @@ mla_status_t mla_prefill_paged(const mla_dims_t* d, const void* q_nope, const vo
   a.kr = reinterpret_cast<uint16_t*>(ws + 2 * kv);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (g_prof.active && 2 * g_prof.used + 1 < static_cast<int>(g_prof.ev.size())) {
-    e0 = g_prof.ev[2 * g_prof.used];
-    e1 = g_prof.ev[2 * g_prof.used + 1];
-    ++g_prof.used;
-  }
   return from_hip(mla::launch_prefill(a, static_cast<hipStream_t>(stream), nullptr, nullptr, e0, e1));
 }
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_prefill_paged(const mla_dims_t* d, const void* q_nope, const void* q_pe,
+                               const int32_t* q_start, int32_t T, int32_t max_q_len, const void* pool,
+                               const float* scales, const int32_t* block_table, int32_t max_pages,
+                               int32_t num_pages, const int32_t* seq_lens, int32_t B, const void* w_uk,
+                               const void* w_uv, void* workspace, size_t ws_bytes, void* out, float* lse,
+                               void* stream) {
+  return prefill_impl(d, q_nope, q_pe, q_start, T, max_q_len, pool, scales, block_table, max_pages, num_pages,
+                      seq_lens, B, w_uk, w_uv, workspace, ws_bytes, out, lse, nullptr, nullptr, stream);
+}
+
+mla_status_t mla_prefill_paged_timed(const mla_dims_t* d, const void* q_nope, const void* q_pe,
+                                     const int32_t* q_start, int32_t T, int32_t max_q_len, const void* pool,
+                                     const float* scales, const int32_t* block_table, int32_t max_pages,
+                                     int32_t num_pages, const int32_t* seq_lens, int32_t B, const void* w_uk,
+                                     const void* w_uv, void* workspace, size_t ws_bytes, void* out, float* lse,
+                                     void* ev_start, void* ev_stop, void* stream) {
+  return prefill_impl(d, q_nope, q_pe, q_start, T, max_q_len, pool, scales, block_table, max_pages, num_pages,
+                      seq_lens, B, w_uk, w_uv, workspace, ws_bytes, out, lse, static_cast<hipEvent_t>(ev_start),
+                      static_cast<hipEvent_t>(ev_stop), stream);
+}
+
+
 
 mla_status_t mla_out_proj(const mla_dims_t* d, const void* o_lat, const void* w_uv, int32_t B,
                           void* out, void* stream) {
@@ -397,44 +417,6 @@ mla_status_t mla_out_proj(const mla_dims_t* d, const void* o_lat, const void* w_
   a.w_uv = static_cast<const uint16_t*>(w_uv);
   a.out = static_cast<uint16_t*>(out);
   return from_hip(mla::launch_out_proj(a, static_cast<hipStream_t>(stream)));
-}
-
-mla_status_t mla_profile_begin(int32_t max_records) {
-  if (max_records <= 0 || g_prof.active) return MLA_ERR_INVALID_ARG;
-  g_prof.ev.assign(2 * static_cast<size_t>(max_records), nullptr);
-  for (auto& e : g_prof.ev) {
-    if (hipEventCreate(&e) != hipSuccess) {
-      for (auto& x : g_prof.ev)
-        if (x) (void)hipEventDestroy(x);
-      g_prof.ev.clear();
-      return MLA_ERR_HIP;
-    }
-  }
-  g_prof.used = 0;
-  g_prof.active = true;
-  return MLA_OK;
-}
-
-mla_status_t mla_profile_end(double* total_ms, int32_t* n_records) {
-  if (!g_prof.active) return MLA_ERR_INVALID_ARG;
-  mla_status_t st = MLA_OK;
-  double sum = 0.0;
-  for (int i = 0; i < g_prof.used; ++i) {
-    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) { st = MLA_ERR_HIP; break; }
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) {
-      st = MLA_ERR_HIP;
-      break;
-    }
-    sum += ms;
-  }
-  if (total_ms) *total_ms = sum;
-  if (n_records) *n_records = g_prof.used;
-  for (auto& e : g_prof.ev) (void)hipEventDestroy(e);
-  g_prof.ev.clear();
-  g_prof.used = 0;
-  g_prof.active = false;
-  return st;
 }
 
 }  // extern "C"

@@ -64,12 +64,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds_ptr) {
 }
 
 // ---- fp8 ------------------------------------------------------------------
-// Two OCP e4m3 codes (byte pair 0-1, or 2-3 with HI) times an fp32 scale,
-// rounded to two bf16.  The codes are converted exactly with the gfx950
-// conversion instruction at scale 1 (its scale operand only takes the power of
-// two part), multiplied by the scale in fp32 and rounded to nearest even.
+// Two OCP e4m3 codes (byte pair 0-1, or 2-3 with HI) as two bf16, exactly:
+// every e4m3 value (3 mantissa bits, exponents -9..8) is a bf16 value.  The
+// gfx950 conversion instruction runs at scale 1 (its scale operand only
+// takes the power-of-two part).
 template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes, float scale) {
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, HI));
+}
+// Two e4m3 codes times an fp32 scale, rounded to two bf16: the codes are
+// converted exactly to fp32 (scale 1), multiplied by the scale in fp32 and
+// rounded to nearest even.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2_scaled(uint32_t codes, float scale) {
   typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
   const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, 1.0f, HI);
   return pack_bf16x2(v[0] * scale, v[1] * scale);
