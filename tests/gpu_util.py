@@ -76,8 +76,12 @@ REL_L2 = 5e-3
 
 
 def assert_close(x, ref, what, max_abs_tol=MAX_ABS, rel_tol=REL_L2):
+    """Checks the bar and prints the achieved margin (`[margin]` lines, shown
+    with pytest -s, are the source of the per-workload margin table)."""
     assert np.all(np.isfinite(x)), f"{what}: non-finite values"
     ma, rl = max_abs(x, ref), rel_l2(x, ref)
+    print(f"[margin] {what}: max_abs={ma:.3e} rel_l2={rl:.3e} (bar {max_abs_tol:g} / {rel_tol:g})",
+          flush=True)
     assert ma <= max_abs_tol and rl <= rel_tol, f"{what}: max_abs={ma:.3e} rel_l2={rl:.3e}"
     return ma, rl
 

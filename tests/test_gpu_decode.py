@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import mla_latent_kv_nope_amd as mla
-from oracle import latent_attention, reference_decode, sequence_rows
+from oracle import (e4m3fn_decode, fp8_cache_codes, latent_attention, reference_decode,
+                    sequence_rows)
 from workload import configs, make_inputs
 from workload.torch_io import bf16_bits, bf16_tensor, i32_tensor
 
@@ -239,15 +240,167 @@ def test_ragged_full_size_sampled():
     _compare(inp, res, batches=pick)
 
 
+def _token_slots(inp):
+    """(page, slot) of every cached token, in token order."""
+    ps = inp.wl.page_size
+    pos = inp.positions()
+    return inp.block_table[inp.seq_ids(), pos // ps], pos % ps
+
+
 @pytest.mark.slow
-def test_fp8long_full_size_sampled():
+def test_fp8long_full_size():
+    # The fp8 workload at full size (B=4, S=131072), in the benchmark's launch
+    # configuration:
+    #  - every cached row's codes and scale against the oracle's encoder
+    #    (mismatch fraction reported; <= 1e-5 allowed: the GPU rotates k_pe
+    #    in fp64 too, but an fp32 result on a rounding boundary may differ);
+    #  - o_lat and lse of every (sequence, head) against the absorbed form
+    #    over the oracle's dequantised rows, driven by the GPU's own query;
+    #  - out of every sequence against the explicit form (the oracle's
+    #    definition) for 8 heads spread over the four scoring waves.
     wl = configs.FP8LONG
     inp = make_inputs(wl)
     d = dims_for(wl)
     print("[decode fp8long full] B=4 H=128 S=131072 fp8", flush=True)
     res = decode_step(inp, d)
     assert np.all(np.isfinite(res["out"]))
-    _compare(inp, res, batches=[2], heads=[0, 77, 127])
+    host = res["pool"].cpu().numpy()
+    hs = res["scales"].cpu().numpy()
+    pages, slots = _token_slots(inp)
+    codes, scale = fp8_cache_codes(inp.c_kv, inp.k_pe, inp.positions(), wl.rope_base)
+    code_mism = float(np.mean(host[pages, slots] != codes))
+    scale_mism = float(np.mean(hs[pages, slots].view(np.uint32) != scale.view(np.uint32)))
+    print(f"[margin] fp8long code mismatch fraction {code_mism:.2e}, scale mismatch {scale_mism:.2e}",
+          flush=True)
+    assert code_mism <= 1e-5 and scale_mism <= 1e-5
+    deq = e4m3fn_decode(codes) * scale.astype(np.float64)[:, None]
+    scale_sm = wl.softmax_scale
+    o_ref = np.empty_like(res["o_lat"])
+    l_ref = np.empty_like(res["lse"])
+    cu = inp.cu_seqlens
+    for b in range(wl.batch):
+        rows = deq[cu[b]:cu[b + 1]]
+        o_ref[b], l_ref[b] = latent_attention(res["q"][b], rows[:, :wl.d_c], rows[:, wl.d_c:], scale_sm)
+    assert_close(res["o_lat"], o_ref, "fp8long o_lat, every head (absorbed form)")
+    lse_err = float(np.max(np.abs(res["lse"] - l_ref)))
+    print(f"[margin] fp8long lse max_abs={lse_err:.3e}", flush=True)
+    assert lse_err <= 1e-2
+    _compare(inp, res, batches=range(wl.batch), heads=[0, 17, 38, 55, 70, 93, 108, 127])
+
+
+def test_softmax_normalises_on_gpu():
+    # c_kv = 1 everywhere (k_pe = 0): o_lat = sum_t p_t = 1 for every head,
+    # within the bf16 rounding of P and of the output (4e-3); bf16 and fp8
+    # caches, split and unsplit
+    for fp8 in (False, True):
+        wl = configs.V3.with_(name="v3_ones", batch=3, seq_len=None, seq_lens=(1, 700, 2100), fp8=fp8)
+        inp = make_inputs(wl)
+        inp.c_kv = np.full_like(inp.c_kv, 0x3F80)              # 1.0
+        inp.k_pe = np.zeros_like(inp.k_pe)
+        d = dims_for(wl)
+        pool, scales, t = build_cache(inp, d)
+        q = mla.absorb_q(d, t["q_nope"], t["q_pe"], t["q_pos"], t["w_uk"])
+        for num_splits in (1, 0):
+            o_lat, _ = mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"],
+                                        num_splits=num_splits)
+            torch.cuda.synchronize()
+            err = float(np.max(np.abs(o_lat.float().cpu().numpy() - 1.0)))
+            print(f"[margin] ones fp8={fp8} splits={num_splits}: max |o_lat - 1| = {err:.3e}", flush=True)
+            assert err <= 4e-3
+
+
+def _delta_inputs(wl, stars):
+    """c_kv column 0 = 0 except 1 at each sequence's starred token; for an fp8
+    cache every row's largest magnitude is exactly 7 (column 1) and the rest
+    stay below it, so every scale is 7/448 = 2^-6 and code * scale is exact in
+    bf16."""
+    inp = make_inputs(wl)
+    c = inp.c_kv.copy()
+    if wl.fp8:
+        from workload import f32_to_bf16_bits
+        from oracle import bf16_bits_to_f64
+        x = np.clip(bf16_bits_to_f64(c), -6.5, 6.5)
+        c = f32_to_bf16_bits(x.astype(np.float32))
+        c[:, 1] = 0x40E0                                   # 7.0
+        k = np.clip(bf16_bits_to_f64(inp.k_pe), -4.5, 4.5)    # rotated pairs stay below 6.4
+        inp.k_pe = f32_to_bf16_bits(k.astype(np.float32))
+    c[:, 0] = 0
+    for b, ts in enumerate(stars):
+        c[inp.cu_seqlens[b] + ts, 0] = 0x3F80               # 1.0
+    inp.c_kv = c
+    return inp
+
+
+def _delta_query(wl):
+    # q = A e_0 with softmax_scale * A * log2(e) > 149: every other token's
+    # weight underflows to 0 in fp32, even after the split pieces' merge
+    q = np.zeros((wl.batch, wl.n_heads, wl.d_c + wl.d_rope), np.uint16)
+    q[:, :, 0] = 0x44D0                                    # 1664.0
+    return q
+
+
+def _piece_first_tiles(seq_lens, num_splits):
+    """Global tile index where each piece of the split plan starts."""
+    tiles = [(s + 31) // 32 for s in seq_lens]
+    total = sum(tiles)
+    quota = -(-total // num_splits)
+    return {w * quota for w in range(num_splits) if w * quota < total}
+
+
+@pytest.mark.parametrize("num_splits", [1, 5])
+def test_fp8_delta_query_redoes_piece_bit_exact(num_splits):
+    # fp8 cache (the general layout): each starred token lies past the first
+    # tile of the piece holding it, so its score exceeds the piece's exponent
+    # offset by far more than 64 (log2) and the piece is recomputed with the
+    # true maximum; o_lat must still be the starred row exactly (code * 2^-6)
+    seq_lens = (300, 1000, 4096, 77)
+    wl = configs.V3.with_(name="v3_fp8_delta", fp8=True, batch=4, seq_len=None, seq_lens=seq_lens)
+    starts = _piece_first_tiles(seq_lens, num_splits)
+    first_tile = np.concatenate([[0], np.cumsum([(s + 31) // 32 for s in seq_lens])])
+    stars = []
+    for b, s in enumerate(seq_lens):
+        # the last token of the sequence in a tile (not its first) that does
+        # not start a piece
+        ok = [tl for tl in range((s - 1) // 32, 0, -1) if first_tile[b] + tl not in starts]
+        assert ok, (b, s)
+        stars.append(min(s - 1, 32 * ok[0] + 31))
+    inp = _delta_inputs(wl, stars)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    o_lat, lse = mla.decode_paged(d, bf16_tensor(_delta_query(wl), DEV), pool, scales, t["block_table"],
+                                  t["seq_lens"], num_splits=num_splits)
+    torch.cuda.synchronize()
+    got = bf16_bits(o_lat)
+    codes, scale = fp8_cache_codes(inp.c_kv, inp.k_pe, inp.positions(), wl.rope_base)
+    assert np.all(scale == np.float32(2.0 ** -6))
+    deq = e4m3fn_decode(codes) * 2.0 ** -6
+    from workload import f32_to_bf16_bits
+    for b, ts in enumerate(stars):
+        want = f32_to_bf16_bits(deq[inp.cu_seqlens[b] + ts, :wl.d_c].astype(np.float32))
+        assert np.array_equal(got[b], np.broadcast_to(want, got[b].shape)), (b, ts)
+    assert np.all(np.isfinite(lse.cpu().numpy()))
+
+
+@pytest.mark.parametrize("t_star", [0, 15, 16, 17, 30, 31, 36])
+def test_tiny_delta_query_one_piece(t_star):
+    # tiny dims, each sequence one piece: a starred token past the first tile
+    # (t_star 36) forces the recompute with the true maximum
+    wl = configs.TINY
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    c = inp.c_kv.copy()
+    c[:, 0] = 0
+    c[t_star, 0] = 0x3F80                                 # sequence 0 holds tokens 0..36
+    inp.c_kv = c
+    pool, scales, t = build_cache(inp, d)
+    q = np.zeros((wl.batch, wl.n_heads, wl.d_c + wl.d_rope), np.uint16)
+    q[:, :, 0] = 0x44D0                                   # 1664.0
+    o_lat, lse = mla.decode_paged(d, bf16_tensor(q, DEV), pool, scales, t["block_table"],
+                                  t["seq_lens"], num_splits=1)
+    torch.cuda.synchronize()
+    got = bf16_bits(o_lat)[0]
+    assert np.array_equal(got, np.broadcast_to(c[t_star], got.shape))
+    assert abs(float(lse[0, 0]) - 1664.0 * wl.softmax_scale) < 1e-3
 
 
 @pytest.mark.parametrize("t_star", [0, 15, 16, 17, 30, 31, 36])

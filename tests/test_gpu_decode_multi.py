@@ -90,11 +90,16 @@ def test_q_len_one_is_decode_paged_bit_for_bit():
 
 
 def test_multi_split_counts():
-    # Every split count meets the oracle bar.  (Between two split counts the
-    # bf16 outputs differ by rounding only, but not within a fixed tighter
-    # bound: with one-tile pieces a 2000-token query merges 63 bf16 partial
-    # outputs, measured 3.1e-3 relative L2 from the single-piece result.)  The
-    # fp32 lse merges exactly up to fp32 rounding.
+    # Every split count meets the oracle bar.  Between two split counts the
+    # o_lat values differ by rounding only: a piece's normalised partial output
+    # is stored as bf16 (one rounding, <= 2^-9 relative) and the merged o_lat
+    # is rounded to bf16 once more, while an unsplit sequence is rounded once.
+    # So two split counts may differ by up to one bf16 step (2^-8 relative)
+    # per value; the relative L2 between them is checked against that and
+    # printed.  (A 2000-token query cut into one-tile pieces merges 63 bf16
+    # partials; the 2e-3 split-invariance bound of the fp32-partial design
+    # does not hold for bf16 partials.)  The fp32 lse merges exactly up to
+    # fp32 rounding.
     wl = configs.V3.with_(name="v3_q3_split", batch=2, seq_len=None, seq_lens=(300, 2000), q_len=3)
     inp = make_inputs(wl)
     d = dims_for(wl)
@@ -103,6 +108,9 @@ def test_multi_split_counts():
     for num_splits in (1, 5):
         got = multi_step(inp, d, num_splits=num_splits, cache=res["cache"])
         _compare(inp, got)
+        rel = float(np.linalg.norm(got["o_lat"] - res["o_lat"]) / np.linalg.norm(res["o_lat"]))
+        print(f"[margin] multi o_lat splits {num_splits} vs auto: rel_l2={rel:.3e} (bound 2^-8)", flush=True)
+        assert rel <= 2.0 ** -8
         assert np.max(np.abs(got["lse"] - res["lse"])) <= 1e-5
 
 

@@ -161,3 +161,42 @@ def test_rows_before_the_buffer_are_skipped():
     ref = reference_prefill(inp, rows=list(range(5, 25)))
     assert_close(out.float().cpu().numpy().astype(np.float64), ref["out"][0], "out")
     assert np.max(np.abs(lse.cpu().numpy() - ref["lse"][0])) <= 1e-2
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("amp", [192.0, 1664.0], ids=["jump20", "jump173"])
+def test_late_key_raises_the_offset(amp, fp8):
+    # One key (t* = 150, key tile 4) scores softmax_scale * amp: W_UK[h] maps
+    # q_nope = amp e_0 onto latent column 0 (column 0 of W_UK[h] is e_0), and
+    # c_kv column 0 is 0 except 1 at t*.  For a query that sees t*, that tile's
+    # maximum exceeds the offset set by the earlier key tiles (all scores 0) by
+    # amp * softmax_scale * log2(e) = 20 or 173 (base 2): the running offset
+    # moves and the earlier O and denominator are rescaled (by 2^-20, or to 0).
+    # Queries before t* see only zero scores.
+    wl = _wl("v3_h4_c120_star", 4, (300,), 120, fp8=fp8)
+    inp = make_inputs(wl)
+    from workload import f32_to_bf16_bits
+    from oracle import bf16_bits_to_f64
+    c = inp.c_kv.copy()
+    if fp8:
+        # every row's largest magnitude is exactly 7 (column 1), so each scale
+        # is 2^-6 and the dequantised rows are exact in bf16: the huge score
+        # carries no rounding of its key
+        c = f32_to_bf16_bits(np.clip(bf16_bits_to_f64(c), -6.5, 6.5).astype(np.float32))
+        c[:, 1] = 0x40E0                                   # 7.0
+        inp.k_pe = f32_to_bf16_bits(np.clip(bf16_bits_to_f64(inp.k_pe), -4.5, 4.5).astype(np.float32))
+    c[:, 0] = 0
+    c[150, 0] = 0x3F80                                     # 1.0
+    inp.c_kv = c
+    w = inp.w_uk.copy()
+    w[:, :, 0] = 0
+    w[:, 0, 0] = 0x3F80                                    # column 0 of W_UK[h] = e_0
+    inp.w_uk = w
+    qn = np.zeros_like(inp.q_nope)
+    qn[..., 0] = f32_to_bf16_bits(np.array([amp], np.float32))[0]
+    inp.q_nope = qn
+    inp.q_pe = np.zeros_like(inp.q_pe)
+    d = dims_for(wl)
+    print(f"[prefill star] amp={amp} fp8={fp8}", flush=True)
+    out, lse, starts, _ = run_prefill(inp, d)
+    compare(inp, out, lse, starts)
