@@ -331,6 +331,31 @@ const char* mla_status_string(mla_status_t status);
 const char* mla_last_hip_error(void);
 
 /*
+ * mla_decode_paged_noalloc - mla_decode_paged_multi without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The workspace is a device array inside the library of
+ * mla_decode_noalloc_max_bytes() = 64 MiB, present on every device the
+ * library is loaded on until the process ends; the call allocates nothing
+ * (it looks the array's address up once per device).  Calls whose
+ * mla_decode_workspace_size(dims, B * q_len, num_splits) exceeds it return
+ * MLA_ERR_WORKSPACE before anything is enqueued (with 128 heads and
+ * automatic splits on 256 compute units: B * q_len up to 254).
+ * All calls on one device share the array: calls that may overlap on one
+ * device (different streams, several threads) race and must not be issued;
+ * every call writes the parts of the array it reads first, so nothing needs
+ * clearing between calls.  Arguments, other errors and results as for
+ * mla_decode_paged_multi.
+ */
+mla_status_t mla_decode_paged_noalloc(const mla_dims_t* dims, const void* q, const void* pool,
+                                      const float* scales, const int32_t* block_table,
+                                      int32_t max_pages, int32_t num_pages, const int32_t* seq_lens,
+                                      int32_t B, int32_t q_len, int32_t num_splits, void* o_lat,
+                                      float* lse, void* stream);
+/* Bytes of the device array mla_decode_paged_noalloc uses as workspace. */
+size_t mla_decode_noalloc_max_bytes(void);
+
+/*
  * mla_decode_paged_timed, mla_prefill_paged_timed - mla_decode_paged_multi and
  * mla_prefill_paged with two caller-owned HIP events (hipEvent_t values
  * created by the caller, or NULL) recorded on `stream` immediately before and

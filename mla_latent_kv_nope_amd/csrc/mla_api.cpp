@@ -223,17 +223,18 @@ mla_status_t decode_impl(const mla_dims_t* d, const void* q, const void* pool, c
                          const int32_t* block_table, int32_t max_pages, int32_t num_pages,
                          const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t num_splits,
                          void* workspace, size_t ws_bytes, void* o_lat, float* lse, hipEvent_t e0,
-                         hipEvent_t e1, void* stream) {
+                         hipEvent_t e1, void* stream, bool use_scratch = false) {
   const mla_status_t st = check_dims(d);
   if (st != MLA_OK) return st;
   if (B <= 0 || max_pages <= 0 || num_pages <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
   if (q_len < 1 || q_len > MLA_MAX_Q_LEN || static_cast<int64_t>(B) * q_len > (int64_t{1} << 24))
     return MLA_ERR_INVALID_ARG;
-  if (!q || !pool || !block_table || !seq_lens || !workspace || !o_lat) return MLA_ERR_INVALID_ARG;
+  if (!q || !pool || !block_table || !seq_lens || (!use_scratch && !workspace) || !o_lat)
+    return MLA_ERR_INVALID_ARG;
   const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
   if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
-      !aligned(workspace, 256) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)) ||
+      (!use_scratch && !aligned(workspace, 256)) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)) ||
       (fp8 && !aligned(scales, 16)))
     return MLA_ERR_INVALID_ARG;
   if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads, fp8)) return MLA_ERR_UNSUPPORTED;
@@ -241,6 +242,14 @@ mla_status_t decode_impl(const mla_dims_t* d, const void* q, const void* pool, c
   const int BQ = B * q_len;                     // query sequences
   const int parts = effective_parts(num_splits, BQ, d->n_heads);
   const mla::WorkspaceLayout L = mla::decode_workspace_layout(BQ, d->n_heads, d->d_c, parts);
+  if (use_scratch) {
+    // the library's device scratch: sizes beyond it are refused before any
+    // HIP call; then its address on the current device
+    if (L.total > mla::kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+    const hipError_t e = mla::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return from_hip(e);
+    ws_bytes = mla::kNoAllocScratchBytes;
+  }
   if (ws_bytes < L.total) return MLA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   mla::DecodeArgs a{};
@@ -287,6 +296,16 @@ mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const vo
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
                      num_splits, workspace, ws_bytes, o_lat, lse, nullptr, nullptr, stream);
 }
+
+mla_status_t mla_decode_paged_noalloc(const mla_dims_t* d, const void* q, const void* pool,
+                                      const float* scales, const int32_t* block_table, int32_t max_pages,
+                                      int32_t num_pages, const int32_t* seq_lens, int32_t B, int32_t q_len,
+                                      int32_t num_splits, void* o_lat, float* lse, void* stream) {
+  return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
+                     num_splits, nullptr, 0, o_lat, lse, nullptr, nullptr, stream, true);
+}
+
+size_t mla_decode_noalloc_max_bytes(void) { return mla::kNoAllocScratchBytes; }
 
 mla_status_t mla_decode_paged_timed(const mla_dims_t* d, const void* q, const void* pool,
                                     const float* scales, const int32_t* block_table, int32_t max_pages,

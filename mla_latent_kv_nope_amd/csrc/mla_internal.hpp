@@ -94,6 +94,12 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts);
+
+// Size of the device scratch array that mla_decode_paged_noalloc uses as its
+// workspace, and its address on the current device (looked up once per
+// device; no allocation).
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+hipError_t noalloc_scratch(void** ptr);
 int decode_auto_parts(int B, int H);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);

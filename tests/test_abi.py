@@ -141,6 +141,33 @@ def test_decode_validation():
     _expect(call(maxp=0), _native.MLA_ERR_INVALID_ARG)
 
 
+def test_decode_noalloc_validation():
+    """mla_decode_paged_noalloc: same argument checks as the decode calls (no
+    workspace argument), and a required workspace above the library's device
+    array is MLA_ERR_WORKSPACE, both before any HIP call."""
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    f = lib.mla_decode_paged_noalloc
+    cap = lib.mla_decode_noalloc_max_bytes()
+    assert cap == 64 << 20
+
+    def call(B=4, q_len=1, ns=8, q=P, o=P, scales=None):
+        return f(ctypes.byref(d), q, P, scales, P, 8, 40, P, B, q_len, ns, o, P, None)
+
+    _expect(call(q=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(o=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(q=P + 8), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(B=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(q_len=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(scales=P), _native.MLA_ERR_INVALID_ARG)
+    # the largest batch that fits the array, and one more query sequence
+    B = 1
+    while lib.mla_decode_workspace_size(ctypes.byref(d), B + 1, 8) <= cap:
+        B += 1
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), B + 1, 8) > cap
+    _expect(call(B=B + 1), _native.MLA_ERR_WORKSPACE)
+    _expect(call(B=(B + 1) // 2 + 1, q_len=2), _native.MLA_ERR_WORKSPACE)
+
+
 def test_decode_multi_validation():
     """mla_decode_paged_multi: q_len range, and a workspace sized for B * q_len
     query sequences."""
