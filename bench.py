@@ -2,8 +2,9 @@
 """Benchmark of one MLA absorbed-decode step on one MI355X.
 
 A step is the whole hot path for one new token per sequence:
-  mla_append_latent (the B new rows) -> mla_absorb_q -> mla_decode_paged
-  (split attention with its own tile plan + LSE combine) -> mla_out_proj,
+  mla_append_latent (the B new rows) -> mla_absorb_q -> mla_decode_paged_out
+  (split attention with its own tile plan, then the LSE merge and the W_UV
+  output projection in one kernel),
 on the DeepSeek-V3-shaped workload (B=64, H=128, d_c=512, d_rope=64,
 d_nope=d_v=128, S=8192, page 64, bf16 latent cache, permuted pages), with all
 inputs resident in HBM.  The cache holds S-1 tokens per sequence before the
@@ -11,8 +12,8 @@ timed region; every step appends token S-1 (the same slot each step) and
 attends over all S tokens.
 
 `--workload v3mtp2` runs the same step for two new tokens per sequence scored
-in one pass (mla_decode_paged_multi; the verification of multi-token-prediction
-drafts); its tokens/s counts the B * q_len scored tokens.
+in one pass (the q_len form of the same call; the verification of
+multi-token-prediction drafts); its tokens/s counts the B * q_len scored tokens.
 
 Prints one JSON line: whole-step decode tokens/s, plus
   roofline: the split-attention kernel's achieved HBM bandwidth
@@ -405,11 +406,13 @@ def main():
                                    t["seq_lens"], args.num_splits, ws, o_lat.view(B, ql, H, wl.d_c),
                                    lse.view(B, ql, H), events=ev)
 
+    # the step: decode with the W_UV projection in its merge kernel (o_lat and
+    # lse are not needed downstream and are not written)
     def step(ev=None):
         mla.append_latent(d, new_c, new_k, new_pos, new_sid, t["block_table"], pool, scales)
         mla.absorb_q(d, q_nope, q_pe, q_pos, t["w_uk"], q)
-        decode(ev)
-        mla.out_proj(d, o_lat, t["w_uv"], out)
+        mla.decode_paged_out(d, q.view(B, ql, H, R), pool, scales, t["block_table"], t["seq_lens"],
+                             t["w_uv"], args.num_splits, ws, out.view(B, ql, H, wl.d_v), events=ev)
 
     for _ in range(args.warmup):
         step()
@@ -485,9 +488,9 @@ def main():
                    "total_tokens": total_tokens,
                    "page_size": wl.page_size, "cache": "fp8_e4m3" if wl.fp8 else "bf16",
                    "num_splits": args.num_splits or "auto",
-                   "step": ("append+absorb+decode(plan,split,combine)+out_proj" if ql == 1 else
-                            f"append({ql} new tokens per sequence)+absorb+decode_multi(plan,split,"
-                            f"combine)+out_proj; value counts the B*q_len new tokens scored")},
+                   "step": ("append+absorb+decode_out(plan,split,merge+W_UV projection)" if ql == 1 else
+                            f"append({ql} new tokens per sequence)+absorb+decode_out(plan,split,"
+                            f"merge+W_UV projection); value counts the B*q_len new tokens scored")},
         "decode_kernel_tokens_per_s": round(BQ / (split_ms * 1e-3), 1),
         "launch": "hip graph replay of the captured step" if args.graph else "eager calls",
         "roofline": roof,

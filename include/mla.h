@@ -304,6 +304,36 @@ mla_status_t mla_decode_paged_multi(const mla_dims_t* dims, const void* q, const
                                     size_t ws_bytes, void* o_lat, float* lse, void* stream);
 
 /*
+ * mla_decode_paged_out - mla_decode_paged_multi and mla_out_proj in one call:
+ * the kernel that merges the split pieces also applies W_UV, with the merged
+ * latent rows of a head still on chip, so o_lat never has to be written and
+ * read back (d_c = 512, d_v = 128 only, else MLA_ERR_UNSUPPORTED).
+ * Source: W_UV absorbed on the output side (sheratonhq.com section 2.1);
+ * operators fused to save memory round trips (agent.csdn.net section 2.3;
+ * zskr.cn section 4.2).
+ *
+ *   w_uv        bf16 [H][d_c][d_v], as for mla_out_proj
+ *   out         bf16 [B][q_len][H][d_v] (written): W_UV[h]^T . o_lat[b][i][h]
+ *   o_lat       bf16 [B][q_len][H][d_c] written when not NULL
+ *   lse         fp32 [B][q_len][H] written when not NULL
+ *   ev_start, ev_stop  caller-owned HIP events (hipEvent_t) recorded
+ *               immediately before and after the split attention kernel, or
+ *               NULL (for measurements)
+ * Other arguments, the workspace size (mla_decode_workspace_size(dims,
+ * B * q_len, num_splits)) and errors as for mla_decode_paged_multi; out NULL
+ * or w_uv NULL is MLA_ERR_INVALID_ARG.  o_lat and lse are bit-equal to those
+ * of mla_decode_paged_multi on the same inputs and split count; out is the
+ * projection of that bf16 o_lat with fp32 accumulation (it may differ from
+ * mla_out_proj's result in the order of the fp32 additions).
+ */
+mla_status_t mla_decode_paged_out(const mla_dims_t* dims, const void* q, const void* pool,
+                                  const float* scales, const int32_t* block_table,
+                                  int32_t max_pages, int32_t num_pages, const int32_t* seq_lens,
+                                  int32_t B, int32_t q_len, int32_t num_splits, const void* w_uv,
+                                  void* workspace, size_t ws_bytes, void* out, void* o_lat,
+                                  float* lse, void* ev_start, void* ev_stop, void* stream);
+
+/*
  * mla_out_proj - apply W_UV on the output side.
  * Source: W_UV is absorbed into the output projection (sheratonhq.com section 2.1).
  *

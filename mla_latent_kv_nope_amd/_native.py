@@ -49,6 +49,7 @@ EXPORTS = (
     "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_last_hip_error",
     "mla_decode_paged_timed", "mla_prefill_paged_timed", "mla_decode_paged_noalloc",
     "mla_decode_noalloc_max_bytes", "mla_prefill_workspace_size", "mla_prefill_paged",
+    "mla_decode_paged_out",
 )
 
 _P = ctypes.c_void_p
@@ -96,6 +97,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged_timed.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P,
                                            ctypes.c_size_t, _P, _P, _P, _P, _P]
     lib.mla_decode_paged_timed.restype = ctypes.c_int
+    lib.mla_decode_paged_out.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P,
+                                         ctypes.c_size_t, _P, _P, _P, _P, _P, _P]
+    lib.mla_decode_paged_out.restype = ctypes.c_int
     lib.mla_decode_paged_noalloc.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P]
     lib.mla_decode_paged_noalloc.restype = ctypes.c_int
     lib.mla_decode_noalloc_max_bytes.argtypes = []

@@ -323,6 +323,59 @@ def decode_paged_noalloc(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: O
     return o_lat, lse
 
 
+def decode_paged_out(d: Dims, q: torch.Tensor, pool: torch.Tensor, scales: Optional[torch.Tensor],
+                     block_table: torch.Tensor, seq_lens: torch.Tensor, w_uv: torch.Tensor,
+                     num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_o_lat: bool = False, want_lse: bool = False,
+                     events=None):
+    """mla_decode_paged_out: decode plus the W_UV projection in one call.  q is
+    [B][H][R] or [B][q_len][H][R]; returns out [.., H, d_v], o_lat [.., H, d_c]
+    (or None) and lse [.., H] (or None), shaped like q's leading dimensions."""
+    H, R = d.n_heads, d.d_c + d.d_rope
+    if q.dim() == 3:
+        B, q_len = q.shape[0], 1
+        lead = (B,)
+    elif q.dim() == 4:
+        B, q_len = q.shape[0], q.shape[1]
+        lead = (B, q_len)
+    else:
+        raise ValueError("q must be [B][H][R] or [B][q_len][H][R]")
+    _req(q, "q", torch.bfloat16, lead + (H, R))
+    num_pages = pool.shape[0]
+    if _is_fp8(d):
+        _req(pool, "pool", torch.uint8, pool_shape(d, num_pages))
+        _req(scales, "scales", torch.float32, (num_pages, d.page_size))
+    else:
+        _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages]")
+    _req(block_table, "block_table", torch.int32)
+    _req(seq_lens, "seq_lens", torch.int32, (B,))
+    _req(w_uv, "w_uv", torch.bfloat16, (H, d.d_c, d.d_v))
+    if workspace is None:
+        workspace = new_workspace(d, B * q_len, num_splits, q.device)
+    _req(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty(lead + (H, d.d_v), dtype=torch.bfloat16, device=q.device)
+    _req(out, "out", torch.bfloat16, lead + (H, d.d_v))
+    if o_lat is None and want_o_lat:
+        o_lat = torch.empty(lead + (H, d.d_c), dtype=torch.bfloat16, device=q.device)
+    if o_lat is not None:
+        _req(o_lat, "o_lat", torch.bfloat16, lead + (H, d.d_c))
+    if lse is None and want_lse:
+        lse = torch.empty(lead + (H,), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _req(lse, "lse", torch.float32, lead + (H,))
+    e0, e1 = _event_handles(events) if events is not None else (None, None)
+    st = lib.mla_decode_paged_out(ctypes.byref(d), _ptr(q), _ptr(pool), _ptr(scales), _ptr(block_table),
+                                  block_table.shape[1], num_pages, _ptr(seq_lens), B, int(q_len),
+                                  int(num_splits), _ptr(w_uv), _ptr(workspace), workspace.numel(),
+                                  _ptr(out), _ptr(o_lat), _ptr(lse), e0, e1, _stream())
+    _check("mla_decode_paged_out", st)
+    return out, o_lat, lse
+
+
 def decode_noalloc_max_bytes() -> int:
     return int(lib.mla_decode_noalloc_max_bytes())
 

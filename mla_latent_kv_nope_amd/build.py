@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 
-SOURCES = ["mla_api.cpp", "k_append.hip", "k_absorb.hip", "k_decode.hip", "noalloc.hip", "k_out_proj.hip", "k_project.hip",
+SOURCES = ["mla_api.cpp", "k_append.hip", "k_absorb.hip", "k_decode.hip", "k_combine.hip", "noalloc.hip",
+           "k_out_proj.hip", "k_project.hip",
            "k_prefill.hip"]
 ARCH = "gfx950"
 FLAGS = [

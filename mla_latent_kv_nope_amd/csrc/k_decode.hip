@@ -8,17 +8,17 @@
 // split into partial results merged by their log-sum-exp is this library's
 // own design; the pages do not describe one.
 //
-// Two kernels, both enqueued on the caller's stream:
+// This file holds the first of two kernels enqueued on the caller's stream:
 //   k_split   every workgroup first derives the plan (tiles per sequence,
 //             32 tokens each; quota = ceil(total tiles / parts)); workgroup w
 //             then takes global tiles [w*quota, (w+1)*quota) of the
 //             concatenated batch; a range may cover the tail of one sequence
 //             and the head of the next.  A piece that is a whole sequence
-//             writes o_lat/lse directly; otherwise the piece's normalised O
-//             (bf16) and lse (fp32) go to slot w + b of the workspace.
-//   k_combine merges the pieces of every split sequence by their log-sum-exp,
-//             in piece order, and writes o_lat = 0, lse = -inf for sequences
-//             with no tokens.
+//             writes o_lat/lse directly (unless o_lat is null); otherwise the
+//             piece's normalised O (bf16 rows [head][d_c]) and lse (fp32) go
+//             to slot w + b of the workspace.
+//   The second (k_combine.hip) merges the pieces by their log-sum-exp, alone
+//   or together with the W_UV output projection.
 //
 // k_split design (gfx950): one workgroup of NW waves holds every head of one
 // sequence piece (NW = 8 for up to 128 heads), so each 32-token tile of
@@ -214,7 +214,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   // workgroup's range [w * quota, (w + 1) * quota).  Thread i sums a chunk of
   // C consecutive sequences; a wave scan plus the wave totals (in the P slots,
   // unused until the first tile) give each chunk's first tile.  Workgroup 0
-  // also stores the prefix sums and the quota for k_combine.
+  // also stores the prefix sums and the quota for the merge kernels.
   // Query sequence v is new token qi = v % q_len of cache sequence cs =
   // v / q_len and sees len_of(cs, qi) tokens (the cache sequence's length less
   // its later new tokens).  (cs, qi) pairs are walked incrementally: one
@@ -360,7 +360,10 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     const int t1 = t0 + tiles_len(S);
     const int lt0 = g - t0, lt1 = min(gend, t1) - t0;
     const int ntiles = lt1 - lt0;
-    const bool whole = (lt0 == 0) && (lt1 == t1 - t0);
+    // a piece that is a whole sequence writes o_lat / lse itself, unless the
+    // caller merges every piece afterwards (o_lat null: merged with the
+    // output projection)
+    const bool whole = a.o_lat != nullptr && (lt0 == 0) && (lt1 == t1 - t0);
     const int32_t* bt = block_table + static_cast<int64_t>(b_cs) * a.max_pages;
     const char* pool = static_cast<const char*>(a.pool);
     const int64_t page_bytes = static_cast<int64_t>(ROWB) << lg;
@@ -592,7 +595,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       }
     };
     // normalised O of this wave's column blocks to o_lat (whole sequence) or
-    // to the piece's partial slot, in accumulator order
+    // to the piece's partial slot, both bf16 rows [head][d_c]
     auto store_o = [&](int cbf, auto& oo) {
       constexpr int NC = sizeof(oo[0]) / sizeof(oo[0][0]);
       const int fl = lane_id_fresh();
@@ -607,46 +610,33 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
           for (int c = 0; c < NC; ++c) oo[hb][c] *= scv;
         }
       }
-      if (whole) {
-        // the tile ring is free: the block goes to LDS as bf16 rows of one
-        // head, then every thread copies whole rows to o_lat with 16-byte
-        // stores.  Rows are 1040 bytes apart, so the rows of a store's four
-        // 16-lane groups (4 rows apart) start 64 bytes apart modulo the 256
-        // bytes of one pass over the banks.
-        constexpr int ROWE = DC + 8;                           // elements per staged row
-        static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::TILE_BYTES, "o_lat staging fits the ring");
-        uint16_t* const st = reinterpret_cast<uint16_t*>(lds);
+      // the tile ring is free: the block goes to LDS as bf16 rows of one
+      // head, then every thread copies whole rows out with 16-byte stores.
+      // Rows are 1040 bytes apart, so the rows of a store's four 16-lane
+      // groups (4 rows apart) start 64 bytes apart modulo the 256 bytes of one
+      // pass over the banks.
+      constexpr int ROWE = DC + 8;                             // elements per staged row
+      static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::TILE_BYTES, "row staging fits the ring");
+      uint16_t* const st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-        for (int hb = 0; hb < NW; ++hb) {
-          if (hb < HB) {
+      for (int hb = 0; hb < NW; ++hb) {
+        if (hb < HB) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int h = hb * 16 + 4 * fq + i;
-#pragma unroll
-              for (int c = 0; c < NC; ++c)
-                st[h * ROWE + 16 * (cbf + c) + f16] = f32_to_bf16_bits(oo[hb][c][i]);
-            }
-          }
-        }
-        __syncthreads();
-        uint4* const dst = reinterpret_cast<uint4*>(a.o_lat + static_cast<int64_t>(b) * H * DC);
-        for (int i = threadIdx.x; i < H * (DC / 8); i += Cfg::THREADS) {
-          const int h = i / (DC / 8), c8 = i - h * (DC / 8);
-          dst[i] = *reinterpret_cast<const uint4*>(st + h * ROWE + 8 * c8);
-        }
-      } else {
-        constexpr uint32_t kBlk = 64 * 8;                      // one 16 x 16 block, bf16
-        const int64_t slot = static_cast<int64_t>(w) + b;
-        const auto rs = make_rsrc(a.part_o + slot * HB * Cfg::VCB * (kBlk / 2), HB * Cfg::VCB * kBlk);
-        const uint32_t voff = static_cast<uint32_t>(fl) * 8;
-#pragma unroll
-        for (int hb = 0; hb < NW; ++hb) {
-          if (hb < HB) {
+          for (int i = 0; i < 4; ++i) {
+            const int h = hb * 16 + 4 * fq + i;
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-              buffer_store_bf16x4(oo[hb][c], rs, voff, (hb * Cfg::VCB + cbf + c) * kBlk);
+              st[h * ROWE + 16 * (cbf + c) + f16] = f32_to_bf16_bits(oo[hb][c][i]);
           }
         }
+      }
+      __syncthreads();
+      uint16_t* const rows = whole ? a.o_lat + static_cast<int64_t>(b) * H * DC
+                                   : a.part_o + (static_cast<int64_t>(w) + b) * (HB * 16) * DC;
+      uint4* const dst = reinterpret_cast<uint4*>(rows);
+      for (int i = threadIdx.x; i < H * (DC / 8); i += Cfg::THREADS) {
+        const int h = i / (DC / 8), c8 = i - h * (DC / 8);
+        dst[i] = *reinterpret_cast<const uint4*>(st + h * ROWE + 8 * c8);
       }
     };
 
@@ -1125,11 +1115,14 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       }
     }
 
-    if (whole) {
-      // o_lat[b]: lane (quad, l16) writes column 16(cb0 + c) + l16 of heads
+    {
+      // o_lat[b] (whole sequence) or the piece's partial slot, bf16 rows
+      // [head][d_c]: lane (quad, l16) writes column 16(cb0 + c) + l16 of heads
       // 16hb + 4quad + i; heads past H get an offset beyond the buffer's
       // range, whose stores the hardware drops
-      const auto rs = make_rsrc(a.o_lat + static_cast<int64_t>(b) * H * DC, H * DC * 2);
+      uint16_t* const rows = whole ? a.o_lat + static_cast<int64_t>(b) * H * DC
+                                   : a.part_o + slot * (HB * 16) * DC;
+      const auto rs = make_rsrc(rows, H * DC * 2);
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb) {
         if (hb < HB) {
@@ -1142,21 +1135,6 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
               __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(f32_to_bf16_bits(o[hb][c][i])), rs,
                                                     vo, 32 * c, 0);
           }
-        }
-      }
-    } else {
-      // Partial piece: normalised O rounded to bf16 in accumulator order
-      // ([head block][column block][lane][4]), one 8-byte store per lane and
-      // block; k_combine merges the pieces.
-      constexpr uint32_t kBlk = 64 * 8;                        // one 16 x 16 block, bf16
-      const auto rs = make_rsrc(a.part_o + slot * HB * Cfg::VCB * (kBlk / 2), HB * Cfg::VCB * kBlk);
-      const uint32_t voff = static_cast<uint32_t>(fl) * 8;
-#pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
-        if (hb < HB) {
-#pragma unroll
-          for (int c = 0; c < CPW; ++c)
-            buffer_store_bf16x4(o[hb][c], rs, voff, (hb * Cfg::VCB + cb0 + c) * kBlk);
         }
       }
     }
@@ -1175,122 +1153,6 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // all waves must be done reading the ring and the shared 1/l before the
     // next piece refills them
     __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Merge of split sequences.  One workgroup per (sequence, 16-head block); wave
-// q handles column blocks [8q, 8q + 8).  The pieces' lse give each head's
-// merged lse and the piece weights exp(lse_p - lse); the pieces' O are read in
-// the split kernel's accumulator order (bf16, 8-byte loads, 512 bytes per wave
-// instruction), all pieces of a group in flight together, and summed in piece
-// order in fp32.  The merged block goes through LDS so that o_lat is written
-// with 16-byte stores.  Sequences with no tokens get o_lat = 0 and lse = -inf;
-// whole-sequence pieces were written by k_split.
-template <int DC>
-__global__ __launch_bounds__(64 * (DC / 128 > 0 ? DC / 128 : 1)) void k_combine(DecodeArgs a) {
-  constexpr int VCB = DC / 16;
-  constexpr int CPW = VCB < 8 ? VCB : 8;   // column blocks per wave
-  constexpr int NWV = VCB / CPW;           // waves
-  constexpr int THREADS = 64 * NWV;
-  constexpr uint32_t kPieceBytes = VCB * 64 * 8;
-  constexpr int ROW = DC + 16;             // LDS row stride (elements): quads land on distinct banks
-  __shared__ __attribute__((aligned(16))) uint16_t tile[16 * ROW];
-  const int H = a.H, HG16 = (H + 15) >> 4;
-  const int gw = blockIdx.x % HG16;
-  const int b = blockIdx.x / HG16;
-  const int lane = threadIdx.x & 63, cq = threadIdx.x >> 6, quad = lane >> 4, l16 = lane & 15;
-  const int hq = gw * 16 + 4 * quad;       // first of this lane's 4 heads
-  const int t0 = a.plan[b], t1 = a.plan[b + 1], quota = a.plan[a.B + 1];
-  const int hn = min(16, H - gw * 16);     // heads of this block
-
-  // block -> o_lat rows of heads gw*16 .. +hn, 16 bytes per store
-  auto flush = [&]() {
-    __syncthreads();
-    uint4* dst = reinterpret_cast<uint4*>(a.o_lat + (static_cast<int64_t>(b) * H + gw * 16) * DC);
-    for (int i = threadIdx.x; i < hn * DC / 8; i += THREADS) {
-      const int h = i / (DC / 8), c8 = i - h * (DC / 8);
-      dst[i] = *reinterpret_cast<const uint4*>(&tile[h * ROW + 8 * c8]);
-    }
-  };
-
-  if (t1 == t0) {
-    for (int i = threadIdx.x; i < 16 * ROW / 8; i += THREADS)
-      reinterpret_cast<uint4*>(tile)[i] = make_uint4(0, 0, 0, 0);
-    flush();
-    if (a.lse != nullptr && threadIdx.x < hn) a.lse[static_cast<int64_t>(b) * H + gw * 16 + threadIdx.x] = -INFINITY;
-    return;
-  }
-  const int wf = t0 / quota, wl = (t1 - 1) / quota;
-  if (wf == wl || gw * 16 >= H) return;
-
-  constexpr int PG = 4;                    // pieces per round trip
-  const int np = wl - wf + 1;
-  const int64_t lse0 = (static_cast<int64_t>(wf) + b) * H;
-  int hc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hc[i] = min(hq + i, H - 1);
-  const uint32_t voff = static_cast<uint32_t>(lane) * 8;
-  auto load_group = [&](int k0, f32x4 (&t)[PG][CPW], f32x4 (&l)[PG]) {
-#pragma unroll
-    for (int k = 0; k < PG; ++k) {
-      const bool ok = k0 + k < np;
-      const int64_t slot = static_cast<int64_t>(wf + (ok ? k0 + k : 0)) + b;
-      const auto rs = make_rsrc(a.part_o + (slot * HG16 + gw) * (kPieceBytes / 2), kPieceBytes);
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) t[k][c] = buffer_load_bf16x4(rs, voff, (cq * CPW + c) * 512);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) l[k][i] = ok ? a.part_lse[lse0 + (k0 + k) * H + hc[i]] : -INFINITY;
-    }
-  };
-  f32x4 mx = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  f32x4 t[PG][CPW], l[PG];
-  load_group(0, t, l);
-  if (np > PG) {          // rare: the maximum over every piece first
-    for (int k0 = PG; k0 < np; k0 += PG) {
-#pragma unroll
-      for (int k = 0; k < PG; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + k < np) mx[i] = fmaxf(mx[i], a.part_lse[lse0 + (k0 + k) * H + hc[i]]);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < PG; ++k)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], l[k][i]);
-  f32x4 acc[CPW];
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < np; k0 += PG) {
-    if (k0 > 0) load_group(k0, t, l);
-#pragma unroll
-    for (int k = 0; k < PG; ++k) {
-      if (k0 + k >= np) break;
-      // unnormalised weights exp(lse_p - max); the sum normalises at the end
-      f32x4 wgt;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wgt[i] = expf(l[k][i] - mx[i]);
-      sum += wgt;
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) acc[c] = (k0 + k == 0) ? t[k][c] * wgt : acc[c] + t[k][c] * wgt;
-    }
-  }
-  f32x4 inv, lse_all;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    inv[i] = 1.0f / sum[i];
-    lse_all[i] = mx[i] + logf(sum[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < CPW; ++c)
-      tile[(4 * quad + i) * ROW + 16 * (cq * CPW + c) + l16] = f32_to_bf16_bits(acc[c][i] * inv[i]);
-  flush();
-  if (a.lse != nullptr && cq == 0 && l16 == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (hq + i < H) a.lse[static_cast<int64_t>(b) * H + hq + i] = lse_all[i];
   }
 }
 
@@ -1342,7 +1204,7 @@ WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {
   return L;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_split_phase(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = hipSuccess;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   // d_c 512: eight waves whatever H (<= 128).  With fewer heads the rows past H
@@ -1364,12 +1226,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hip
   }
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-  const int hg16 = (a.H + 15) / 16;
-  if (a.d_c == 512)
-    hipLaunchKernelGGL(k_combine<512>, dim3(a.B * hg16), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_combine<32>, dim3(a.B * hg16), dim3(64), 0, s, a);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -222,22 +222,27 @@ namespace {
 mla_status_t decode_impl(const mla_dims_t* d, const void* q, const void* pool, const float* scales,
                          const int32_t* block_table, int32_t max_pages, int32_t num_pages,
                          const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t num_splits,
-                         void* workspace, size_t ws_bytes, void* o_lat, float* lse, hipEvent_t e0,
-                         hipEvent_t e1, void* stream, bool use_scratch = false) {
+                         void* workspace, size_t ws_bytes, void* o_lat, float* lse, const void* w_uv,
+                         void* out, hipEvent_t e0, hipEvent_t e1, void* stream, bool use_scratch = false) {
   const mla_status_t st = check_dims(d);
   if (st != MLA_OK) return st;
   if (B <= 0 || max_pages <= 0 || num_pages <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
   if (q_len < 1 || q_len > MLA_MAX_Q_LEN || static_cast<int64_t>(B) * q_len > (int64_t{1} << 24))
     return MLA_ERR_INVALID_ARG;
-  if (!q || !pool || !block_table || !seq_lens || (!use_scratch && !workspace) || !o_lat)
+  // with `out`, the merge kernel also applies W_UV and o_lat is optional
+  const bool proj = out != nullptr;
+  if (!q || !pool || !block_table || !seq_lens || (!use_scratch && !workspace) || (!proj && !o_lat) ||
+      (proj && !w_uv))
     return MLA_ERR_INVALID_ARG;
   const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
   if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
-      (!use_scratch && !aligned(workspace, 256)) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)) ||
-      (fp8 && !aligned(scales, 16)))
+      (!use_scratch && !aligned(workspace, 256)) || (o_lat && !aligned(o_lat, 16)) ||
+      (lse && !aligned(lse, 4)) || (fp8 && !aligned(scales, 16)) || (proj && !aligned(w_uv, 16)) ||
+      (proj && !aligned(out, 16)))
     return MLA_ERR_INVALID_ARG;
   if (!mla::decode_supported(d->d_c, d->d_rope, d->n_heads, fp8)) return MLA_ERR_UNSUPPORTED;
+  if (proj && !mla::combine_proj_supported(d->d_c, d->d_v)) return MLA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_UNSUPPORTED;
   const int BQ = B * q_len;                     // query sequences
   const int parts = effective_parts(num_splits, BQ, d->n_heads);
@@ -272,9 +277,21 @@ mla_status_t decode_impl(const mla_dims_t* d, const void* q, const void* pool, c
   a.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
   a.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse_off);
-  a.o_lat = static_cast<uint16_t*>(o_lat);
-  a.lse = lse;
-  return from_hip(mla::launch_decode(a, static_cast<hipStream_t>(stream), e0, e1));
+  // the split kernel writes whole sequences to o_lat itself only without the
+  // projection; with it every piece goes to the workspace
+  a.o_lat = proj ? nullptr : static_cast<uint16_t*>(o_lat);
+  a.lse = proj ? nullptr : lse;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_split_phase(a, s, e0, e1);
+  if (e != hipSuccess) return from_hip(e);
+  if (proj) {
+    a.o_lat = static_cast<uint16_t*>(o_lat);
+    a.lse = lse;
+    e = mla::launch_combine_proj(a, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), s);
+  } else {
+    e = mla::launch_combine(a, s);
+  }
+  return from_hip(e);
 }
 
 }  // namespace
@@ -285,7 +302,7 @@ mla_status_t mla_decode_paged(const mla_dims_t* d, const void* q, const void* po
                               int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
                               float* lse, void* stream) {
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, 1, num_splits,
-                     workspace, ws_bytes, o_lat, lse, nullptr, nullptr, stream);
+                     workspace, ws_bytes, o_lat, lse, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const void* pool,
@@ -294,7 +311,7 @@ mla_status_t mla_decode_paged_multi(const mla_dims_t* d, const void* q, const vo
                                     int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
                                     float* lse, void* stream) {
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
-                     num_splits, workspace, ws_bytes, o_lat, lse, nullptr, nullptr, stream);
+                     num_splits, workspace, ws_bytes, o_lat, lse, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 mla_status_t mla_decode_paged_noalloc(const mla_dims_t* d, const void* q, const void* pool,
@@ -302,7 +319,7 @@ mla_status_t mla_decode_paged_noalloc(const mla_dims_t* d, const void* q, const 
                                       int32_t num_pages, const int32_t* seq_lens, int32_t B, int32_t q_len,
                                       int32_t num_splits, void* o_lat, float* lse, void* stream) {
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
-                     num_splits, nullptr, 0, o_lat, lse, nullptr, nullptr, stream, true);
+                     num_splits, nullptr, 0, o_lat, lse, nullptr, nullptr, nullptr, nullptr, stream, true);
 }
 
 size_t mla_decode_noalloc_max_bytes(void) { return mla::kNoAllocScratchBytes; }
@@ -313,8 +330,20 @@ mla_status_t mla_decode_paged_timed(const mla_dims_t* d, const void* q, const vo
                                     int32_t num_splits, void* workspace, size_t ws_bytes, void* o_lat,
                                     float* lse, void* ev_start, void* ev_stop, void* stream) {
   return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
-                     num_splits, workspace, ws_bytes, o_lat, lse, static_cast<hipEvent_t>(ev_start),
-                     static_cast<hipEvent_t>(ev_stop), stream);
+                     num_splits, workspace, ws_bytes, o_lat, lse, nullptr, nullptr,
+                     static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop), stream);
+}
+
+mla_status_t mla_decode_paged_out(const mla_dims_t* d, const void* q, const void* pool,
+                                  const float* scales, const int32_t* block_table, int32_t max_pages,
+                                  int32_t num_pages, const int32_t* seq_lens, int32_t B, int32_t q_len,
+                                  int32_t num_splits, const void* w_uv, void* workspace, size_t ws_bytes,
+                                  void* out, void* o_lat, float* lse, void* ev_start, void* ev_stop,
+                                  void* stream) {
+  if (out == nullptr) return MLA_ERR_INVALID_ARG;
+  return decode_impl(d, q, pool, scales, block_table, max_pages, num_pages, seq_lens, B, q_len,
+                     num_splits, workspace, ws_bytes, o_lat, lse, w_uv, out,
+                     static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop), stream);
 }
 
 size_t mla_prefill_workspace_size(const mla_dims_t* d, int32_t B, int32_t max_pages) {

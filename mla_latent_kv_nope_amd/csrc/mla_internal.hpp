@@ -62,8 +62,8 @@ struct OutProjArgs {
 
 // Workspace of mla_decode_paged, carved from the caller's buffer:
 //   plan      int32 [B + 1] tile prefix sums, then int32 quota
-//   part_o    bf16 [num_parts + B][ceil(H/16)][d_c/16][64][4]  normalised partial
-//             outputs in the decode waves' accumulator order
+//   part_o    bf16 [num_parts + B][16 ceil(H/16)][d_c]  normalised partial
+//             outputs, one row per head
 //   part_lse  fp32 [num_parts + B][H]
 // A partial computed by workgroup w for sequence b lives in slot w + b.
 //
@@ -106,9 +106,17 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_down(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t s);
-// plan + split kernel + combine; `ev0`/`ev1` (may be null) are recorded
-// immediately before and after the split kernel.
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// split kernel (with its plan); `ev0`/`ev1` (may be null) are recorded
+// immediately before and after it.  With a.o_lat null every piece, a whole
+// sequence included, goes to its partial slot.
+hipError_t launch_split_phase(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// merge of split sequences into a.o_lat / a.lse
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+// merge of every sequence (after a split phase with o_lat null) and the
+// projection out[b][h] = W_UV[h]^T o_lat[b][h]; writes a.o_lat, a.lse when
+// not null
+hipError_t launch_combine_proj(const DecodeArgs& a, const uint16_t* w_uv, uint16_t* out, hipStream_t s);
+bool combine_proj_supported(int d_c, int d_v);
 
 bool decode_supported(int d_c, int d_rope, int H, bool fp8);
 bool absorb_supported(int d_c, int d_nope);

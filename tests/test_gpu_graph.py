@@ -1,4 +1,5 @@
-"""The decode step (append -> absorb -> decode -> out-projection) captured in a
+"""The decode step (append -> absorb -> decode -> out-projection, or with the
+out-projection in the decode call's merge kernel) captured in a
 HIP graph and replayed: the library only enqueues kernels on the caller's
 stream (no allocation, no host synchronisation, no memset), so the step can be
 captured as is.  Every replay, with eager work and synchronisations between
@@ -23,8 +24,9 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["decode+out_proj", "decode_out"])
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
-def test_captured_step_replays_bit_for_bit(wl):
+def test_captured_step_replays_bit_for_bit(wl, fused):
     inp = make_inputs(wl)
     d = dims_for(wl)
     t = to_device(inp, DEV)
@@ -52,8 +54,12 @@ def test_captured_step_replays_bit_for_bit(wl):
         mla.append_latent(d, new["c_kv"], new["k_pe"], new["positions"], new["seq_ids"],
                           t["block_table"], pool, scales)
         mla.absorb_q(d, q_nope, t["q_pe"], t["q_pos"], t["w_uk"], q)
-        mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], 0, ws, o_lat, lse)
-        mla.out_proj(d, o_lat, t["w_uv"], out)
+        if fused:
+            mla.decode_paged_out(d, q, pool, scales, t["block_table"], t["seq_lens"], t["w_uv"], 0, ws,
+                                 out, o_lat, lse)
+        else:
+            mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], 0, ws, o_lat, lse)
+            mla.out_proj(d, o_lat, t["w_uv"], out)
 
     def snapshot():
         return [x.clone() for x in (q, o_lat, lse, out)]
