@@ -353,8 +353,10 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void*
  */
 size_t mla_cache_bytes_per_token(const mla_dims_t* dims);
 
-/* Human-readable name of a status code (static storage). */
-const char* mla_status_string(mla_status_t status);
+/* Human-readable name of a status code (static storage); any value is
+ * accepted (an int, so that a code outside the enumeration is not an invalid
+ * enum value), unknown ones give "MLA_ERR_UNKNOWN". */
+const char* mla_status_string(int32_t status);
 
 /* Description of the HIP error behind the calling thread's most recent
  * MLA_ERR_HIP (static storage; "no HIP error" if there was none). */

@@ -13,7 +13,9 @@ import os
 import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIB_PATH selects another build of the same library (the sanitized build
+# of the host-only ABI tests); by default the in-tree libmla.so
+LIB_PATH = os.environ.get("MLA_LIB_PATH") or os.path.join(_HERE, "libmla.so")
 
 
 class Dims(ctypes.Structure):

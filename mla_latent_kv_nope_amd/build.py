@@ -1,9 +1,13 @@
 """Build libmla.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m mla_latent_kv_nope_amd.build [--asm]
+    python -m mla_latent_kv_nope_amd.build [--asm] [--sanitized]
 
 `--asm` also writes the device assembly of every kernel file next to the
 object files under _build/ (used to check register use and instruction mix).
+`--sanitized` also builds _build/asan/libmla.so: the same kernels with the C
+ABI layer (mla_api.cpp) compiled with AddressSanitizer and
+UndefinedBehaviorSanitizer, for the host-only ABI tests (load it with the
+sanitizer runtime preloaded; see tests/test_abi_sanitized.py).
 """
 from __future__ import annotations
 
@@ -59,6 +63,53 @@ def _compile(src: str, asm: bool) -> str:
     return obj
 
 
+# host-side sanitizers for the ABI layer (it has no device code)
+SAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer").split()
+SAN_LIB = os.path.join(BUILD, "asan", "libmla.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime (it also carries the
+    UndefinedBehaviorSanitizer handlers), to be preloaded by the process that
+    loads SAN_LIB."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isfile(path):
+        raise RuntimeError("clang's libclang_rt.asan-x86_64.so not found")
+    return path
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """SAN_LIB: the kernel objects of build() linked with a sanitized
+    mla_api.o (the objects are rebuilt first unless each is newer than every
+    source and header)."""
+    newest = max(os.path.getmtime(os.path.join(CSRC, f)) for f in os.listdir(CSRC))
+    objs_ok = all(os.path.exists(o) and os.path.getmtime(o) >= newest
+                  for o in (os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES))
+    if not objs_ok:
+        build(verbose=False)
+    san_dir = os.path.dirname(SAN_LIB)
+    os.makedirs(san_dir, exist_ok=True)
+    api_obj = os.path.join(san_dir, "mla_api.o")
+    cmd = [hipcc(), *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, "mla_api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized mla_api.cpp:\n{r.stderr}")
+    objs = [api_obj] + [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES
+                        if s != "mla_api.cpp"]
+    tmp = SAN_LIB + ".tmp"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 def build(asm: bool = False, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
@@ -77,9 +128,12 @@ def build(asm: bool = False, verbose: bool = True) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--asm", action="store_true")
+    ap.add_argument("--sanitized", action="store_true")
     args = ap.parse_args()
     try:
         build(asm=args.asm)
+        if args.sanitized:
+            build_sanitized()
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)

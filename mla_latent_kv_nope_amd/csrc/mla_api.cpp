@@ -57,7 +57,7 @@ int effective_parts(int32_t num_splits, int B, int H) {
 
 extern "C" {
 
-const char* mla_status_string(mla_status_t s) {
+const char* mla_status_string(int32_t s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";

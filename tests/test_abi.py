@@ -187,6 +187,32 @@ def test_decode_multi_validation():
     _expect(call(q=P + 8), _native.MLA_ERR_INVALID_ARG)          # q not 16-byte aligned
 
 
+def test_decode_out_validation():
+    """mla_decode_paged_out: out and w_uv required, o_lat and lse optional,
+    the fused merge exists for d_c 512 / d_v 128 only."""
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    f = lib.mla_decode_paged_out
+    B, ql = 4, 2
+    need = lib.mla_decode_workspace_size(ctypes.byref(d), B * ql, 0)
+
+    def call(dims=d, q=P, w=P, wsb=need, out=P, o=None, lse=None, q_len=ql, B=B):
+        return f(ctypes.byref(dims), q, P, None, P, 8, 40, P, B, q_len, 0, w, P, wsb, out, o, lse,
+                 None, None, None)
+
+    _expect(call(out=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(w=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(out=P + 8), _native.MLA_ERR_INVALID_ARG)         # out not 16-byte aligned
+    _expect(call(w=P + 8), _native.MLA_ERR_INVALID_ARG)           # w_uv not 16-byte aligned
+    _expect(call(o=P + 8), _native.MLA_ERR_INVALID_ARG)           # o_lat not 16-byte aligned
+    _expect(call(lse=P + 2), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(q=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(q_len=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(B=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(wsb=need - 1), _native.MLA_ERR_WORKSPACE)
+    tiny = mla.make_dims(4, 32, 16, 16, 16, 16)
+    _expect(call(dims=tiny, wsb=1 << 30), _native.MLA_ERR_UNSUPPORTED)
+
+
 def test_binding_rejects_host_tensors():
     import torch
     d = mla.make_dims(4, 32, 16, 16, 16, 16)
