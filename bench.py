@@ -57,6 +57,9 @@ def parse():
                          "alone for one decode step's new tokens (B=64, d_model=7168, V3 rows); "
                          "prefill: mla_prefill_paged on a 4096-token chunk of two 8192-token "
                          "sequences (V3 heads)")
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="only time the fp64 oracle on a bounded sample of every workload (host "
+                         "cores, no GPU) and print one JSON line per workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three device-to-device copies of MIB MiB (a kernel of known "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -84,6 +87,8 @@ def measured_traffic(workload: str):
     import hashlib
     import re
     name = {"v3": "k_split_v3_b64_s8192.md", "v3mtp2": "k_split_v3mtp2_b64_q2_s8192.md",
+            "v2lite": "k_split_v2lite_b16_s4096.md", "ragged": "k_split_ragged_b128_s512-32768.md",
+            "fp8long": "k_split_fp8long_b4_s131072.md",
             "v3prefill": "k_prefill_v3_b2_s8192_c4096.md"}.get(workload)
     if name is None:
         return None
@@ -333,10 +338,45 @@ def flushed_decode_times(mla, torch, decode, iters: int):
             "note": "split + combine, each call after reading 768 MiB of other data"}
 
 
+# sequences of each workload the oracle decodes for --cpu-baseline-all (about
+# 5-15 s of host time each)
+CPU_SAMPLE_ALL = {"v2lite": 16, "v3": 24, "ragged": 16, "fp8long": 1, "v3mtp2": 12}
+
+
+def cpu_baseline_all():
+    """The oracle as it stands, timed on every workload's bounded sample in one
+    run (the default bench line carries only its own workload's)."""
+    from workload import configs, make_inputs
+    for name, n_seq in CPU_SAMPLE_ALL.items():
+        inp = make_inputs(configs.get(name))
+        # a sample under 5 s (the whole small workload) is repeated and averaged
+        runs, spent = [], 0.0
+        while spent < 5.0:
+            t0 = time.perf_counter()
+            runs.append(cpu_baseline(inp, n_seq))
+            spent += time.perf_counter() - t0
+        base = dict(runs[-1])
+        base["value"] = sum(r["value"] for r in runs) / len(runs)
+        if len(runs) > 1:
+            base["sample"] += f"; mean of {len(runs)} runs"
+        rec = {"workload": name, "description": inp.wl.description, "cpu_baseline": base}
+        print(json.dumps(rec), flush=True)
+        del inp
+    from workload import configs as c
+    wl = c.V3.with_(name="v3prefill", batch=2, seq_len=8192, q_len=4096)
+    inp = make_inputs(wl)
+    print(json.dumps({"workload": "v3prefill", "description": "prefill chunk of 4096 new tokens in "
+                      "two 8192-token sequences, H=128", "cpu_baseline": cpu_baseline_prefill(inp)}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
+        return
+    if args.cpu_baseline_all:
+        cpu_baseline_all()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; the decode path shards by sequence "
