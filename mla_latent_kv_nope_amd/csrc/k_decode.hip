@@ -165,7 +165,10 @@ __device__ __forceinline__ void sched_interleave() {
 __device__ __forceinline__ int clamp_len(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
 
 // ---------------------------------------------------------------------------
-template <int DC, int DR, int NW, bool FP8>
+// HBC (specialised layout only): 16-head blocks whose scores and O are
+// computed, ceil(H / 16) rounded up to 1 or NW; the general layout always
+// computes NW blocks.
+template <int DC, int DR, int NW, bool FP8, int HBC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu((NW + 3) / 4, (NW + 3) / 4)))
 void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict__ seq_lens,
@@ -545,6 +548,12 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // PV(it - 1).
     constexpr int QH = 32, NQW = 4, QCB = 2, PCB = 6;
     constexpr int AHEAD = Cfg::NBUF - 2;
+    // head blocks computed (HBC), 16-head groups per scoring wave (NG), and
+    // the scoring waves' K reads in flight (each feeds NG MFMAs; one group
+    // leaves the registers for more)
+    static_assert(HBC == 1 || HBC == NW, "head blocks computed: 1 or all");
+    constexpr int NG = HBC == 1 ? 1 : 2;
+    constexpr int QD = NG == 1 ? 6 : kQk2Ahead;
     static_assert(NQW * QH == 16 * NW && NQW * QCB + (NW - NQW) * PCB == Cfg::VCB && Cfg::BLOCKED &&
                   Cfg::LW == NW - NQW && Cfg::INSTR % Cfg::LW == 0 && AHEAD >= 1, "specialised shape");
     const bool qkw = wave < NQW;
@@ -581,14 +590,14 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         vb[c] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
       const char* pa_base = pbuf + pslot * PSLOT + p_lane_off();
-      constexpr int AD = 3;
+      constexpr int AD = HBC < 3 ? HBC : 3;
       bf16x8 abuf[AD];
 #pragma unroll
       for (int i = 0; i < AD; ++i) abuf[i] = *reinterpret_cast<const bf16x8*>(pa_base + i * 16 * PROW);
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
+      for (int hb = 0; hb < HBC; ++hb) {
         const bf16x8 pa = abuf[hb % AD];
-        if (hb + AD < NW) abuf[hb % AD] = *reinterpret_cast<const bf16x8*>(pa_base + (hb + AD) * 16 * PROW);
+        if (hb + AD < HBC) abuf[hb % AD] = *reinterpret_cast<const bf16x8*>(pa_base + (hb + AD) * 16 * PROW);
 #pragma unroll
         for (int c = 0; c < NC; ++c) oo[hb][c] = mfma16(pa, vb[c], oo[hb][c]);
         __builtin_amdgcn_sched_barrier(0);
@@ -601,7 +610,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       const int fl = lane_id_fresh();
       const int fq = fl >> 4, f16 = fl & 15;
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
+      for (int hb = 0; hb < HBC; ++hb) {
         if (hb < HB) {
           f32x4 scv;
 #pragma unroll
@@ -619,7 +628,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::TILE_BYTES, "row staging fits the ring");
       uint16_t* const st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
+      for (int hb = 0; hb < HBC; ++hb) {
         if (hb < HB) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -642,11 +651,14 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
 
     if (qkw) {
       const int hq = QH * wave;                   // first head of this wave
-      // Q of two 16-head groups g: lane holds head hq + 16g + l16, elements
+      // a wave whose heads are all past the computed blocks only takes part
+      // in the barriers and its (empty) share of O
+      const bool scores = hq < 16 * HBC;
+      // Q of NG 16-head groups g: lane holds head hq + 16g + l16, elements
       // [32kc + 8quad, +8) of chunk kc
-      bf16x8 qg[2][Cfg::K32];
+      bf16x8 qg[NG][Cfg::K32];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         const int h = hq + 16 * g + l16;
         const bool hv = h < H;
         const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * H + (hv ? h : 0)) * R + 8 * quad;
@@ -657,7 +669,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
           qg[g][kc] = hv ? v : z;
         }
       }
-      f32x4 oo[NW][QCB];
+      f32x4 oo[HBC][QCB];
       float m_use[2] = {-INFINITY, -INFINITY};   // exponent offset per head group (set by the first tile)
       // this lane's largest exponent argument (score . scale_log2 - offset)
       // since the offset was set: the overflow test and, for a recompute, the
@@ -680,8 +692,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
                                                    1024 * (kc >> 1));
           };
           constexpr int NQ = 2 * Cfg::K32;
-          constexpr int QD = kQk2Ahead;
-          f32x4 sacc[2][2] = {};
+          f32x4 sacc[NG][2] = {};
           bf16x8 abuf[QD];
 #pragma unroll
           for (int i = 0; i < QD; ++i) abuf[i] = *a_ptr(i);
@@ -689,14 +700,14 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
           for (int i = 0; i < NQ; ++i) {
             const bf16x8 av = abuf[i % QD];
             if (i + QD < NQ) abuf[i % QD] = *a_ptr(i + QD);
-            sacc[0][i & 1] = mfma16(av, qg[0][i >> 1], sacc[0][i & 1]);
-            sacc[1][i & 1] = mfma16(av, qg[1][i >> 1], sacc[1][i & 1]);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) sacc[g][i & 1] = mfma16(av, qg[g][i >> 1], sacc[g][i & 1]);
             __builtin_amdgcn_sched_barrier(0);
           }
           const uint32_t poff = p_lane_off();
           // sacc[g][tbk][i] is token 16tbk + 4quad + i of head hq + 16g + l16
 #pragma unroll
-          for (int g = 0; g < 2; ++g) {
+          for (int g = 0; g < NG; ++g) {
             float x[8];
 #pragma unroll
             for (int tbk = 0; tbk < 2; ++tbk)
@@ -727,6 +738,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
                 __builtin_bit_cast(bf16x8, pu);
           }
         };
+        if (!scores) return;
         if (tok0 + kTile <= S)
           body(std::false_type{});
         else
@@ -735,7 +747,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
 
       for (int pass = 0;; ++pass) {
 #pragma unroll
-        for (int hb = 0; hb < NW; ++hb)
+        for (int hb = 0; hb < HBC; ++hb)
 #pragma unroll
           for (int c = 0; c < QCB; ++c) oo[hb][c] = f32x4{};
         l_part[0] = l_part[1] = 0.f;
@@ -752,12 +764,12 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         const bool again = vote_again(y_max[0] > kHeadroom || y_max[1] > kHeadroom);
         if (!again || pass > 0) break;   // the second pass starts at the true maximum
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < NG; ++g)
           m_use[g] += max_across_half_waves(max_across_quarter_pairs(y_max[g]));
       }
       // 1/l and lse of this wave's heads (four lanes hold a head)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         const float l_tot = sum_across_half_waves(sum_across_quarter_pairs(l_part[g]));
         const float lse_nat = (m_use[g] + log2f(l_tot)) * kLn2;
         const int h = hq + 16 * g + l16;
@@ -776,10 +788,10 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       store_o(QCB * wave, oo);
     } else {
       const int cbf = NQW * QCB + PCB * (wave - NQW);
-      f32x4 oo[NW][PCB];
+      f32x4 oo[HBC][PCB];
       for (int pass = 0;; ++pass) {
 #pragma unroll
-        for (int hb = 0; hb < NW; ++hb)
+        for (int hb = 0; hb < HBC; ++hb)
 #pragma unroll
           for (int c = 0; c < PCB; ++c) oo[hb][c] = f32x4{};
 #pragma unroll
@@ -1156,9 +1168,9 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   }
 }
 
-template <int DC, int DR, int NW, bool FP8 = false>
+template <int DC, int DR, int NW, bool FP8 = false, int HBC = NW>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_split<DC, DR, NW, FP8>), dim3(a.num_parts), dim3(64 * NW), 0, s, a,
+  hipLaunchKernelGGL((k_split<DC, DR, NW, FP8, HBC>), dim3(a.num_parts), dim3(64 * NW), 0, s, a,
                      a.plan, a.seq_lens, a.block_table);
   return hipGetLastError();
 }
@@ -1217,7 +1229,9 @@ hipError_t launch_split_phase(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0
   } else if (a.fp8) {
     return hipErrorInvalidValue;
   } else if (a.d_c == 512 && a.d_rope == 64) {
-    e = launch_split<512, 64, 8>(a, s);
+    // up to 16 heads: only the first head block is scored and accumulated
+    if (a.H <= 16) e = launch_split<512, 64, 8, false, 1>(a, s);
+    else e = launch_split<512, 64, 8>(a, s);
   } else if (a.d_c == 32 && a.d_rope == 16) {
     if (a.H <= 16) e = launch_split<32, 16, 1>(a, s);
     else e = launch_split<32, 16, 2>(a, s);
