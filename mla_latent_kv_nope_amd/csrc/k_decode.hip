@@ -483,7 +483,10 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // 1 KB copy block lies in one 16-row half of the tile, hence in one page.
     const uint8_t* const pool8 = static_cast<const uint8_t*>(a.pool);
     const int64_t page_bytes8 = static_cast<int64_t>(R) << lg;
-    auto issue_tile8 = [&](int lt, int sslot) {
+    // The NWV waves wv = 0 .. NWV - 1 share a tile's copies (the last one also
+    // copies the scales).
+    auto issue_tile8 = [&](int lt, int sslot, auto nwv_t, int wv) {
+      constexpr int NWV = decltype(nwv_t)::value;
       const int tok0 = lt * kTile;
       char* dst = stage + sslot * Cfg::F8_SLOT;
       const int pg0 = page_id(tok0);
@@ -493,8 +496,8 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       const uint8_t* row0 = ok0 ? pool8 + pg0 * page_bytes8 + (tok0 & (ps - 1)) * R : pool8;
       const int l = lane_id_fresh();
 #pragma unroll
-      for (int j = 0; j < (Cfg::F8_BLK + NW - 1) / NW; ++j) {
-        const int blk = j * NW + wave;
+      for (int j = 0; j < (Cfg::F8_BLK + NWV - 1) / NWV; ++j) {
+        const int blk = j * NWV + wv;
         if (blk < Cfg::F8_BLK) {
           const int b = blk * 1024 + 16 * l;
           const int r = b / R, c = b - r * R;
@@ -505,7 +508,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
           lds_dma16_v(src, lds_addr(dst + blk * 1024));
         }
       }
-      if (wave == NW - 1 && l < kTile / 4) {       // scales of tokens 4l .. 4l + 3
+      if (wv == NWV - 1 && l < kTile / 4) {        // scales of tokens 4l .. 4l + 3
         const float* sc = a.scales;
         const bool hi = 4 * l >= 16;
         const int pg = hi ? pg1 : pg0;
@@ -515,27 +518,45 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         lds_dma16_v(src, lds_addr(dst + Cfg::F8_TILE));
       }
     };
-    // vector memory operations one wave issues per fp8 tile
-    const int ld8 = (Cfg::F8_BLK - wave + NW - 1) / NW + (wave == NW - 1 ? 1 : 0);
+    // vector memory operations copying wave wv of NWV issues per fp8 tile
+    auto ld8_of = [](int nwv, int wv) { return (Cfg::F8_BLK - wv + nwv - 1) / nwv + (wv == nwv - 1 ? 1 : 0); };
     // staging slot -> bf16 ring slot: 8 codes (one bf16 chunk) per unit,
-    // dequantised as code * scale and rounded to bf16 by the gfx950
-    // conversion instruction; rows past the sequence take row 0's scale
-    auto convert8 = [&](int lt, int sslot, int bslot) {
+    // converted exactly to bf16 by the gfx950 conversion instruction at scale
+    // 1, by the nwv waves wv = 0 .. nwv - 1 (units wv * 64 + lane + k * nwv *
+    // 64; the lane index is taken fresh so that no per-unit address is held
+    // across the tile loop); the tile's scales go to scl[bslot]
+    auto convert8 = [&](int lt, int sslot, int bslot, auto nwv_t, int wv) {
+      constexpr int NWV = decltype(nwv_t)::value;
+      constexpr int UPR = R / 8;                    // units per row
+      constexpr int NU = (kTile * UPR + 64 * NWV - 1) / (64 * NWV);   // units per lane
       const int tok0 = lt * kTile;
       const char* src = stage + sslot * Cfg::F8_SLOT;
       const float* sls = reinterpret_cast<const float*>(src + Cfg::F8_TILE);
       char* dst = lds + bslot * Cfg::TILE_BYTES;
-      constexpr int UPR = R / 8;                    // units per row
-      for (int u = threadIdx.x; u < kTile * UPR; u += Cfg::THREADS) {
-        const int r = u / UPR, c = u - r * UPR;
-        const uint2 x = *reinterpret_cast<const uint2*>(src + r * R + 8 * c);
-        const uint4 y = {fp8x2_to_bf16x2<false>(x.x), fp8x2_to_bf16x2<true>(x.x),
-                         fp8x2_to_bf16x2<false>(x.y), fp8x2_to_bf16x2<true>(x.y)};
-        *reinterpret_cast<uint4*>(dst + lds_off<Cfg>(r, c)) = y;
+      const int u0 = wv * 64 + lane_id_fresh();
+      // every unit's codes are read first, then converted and written
+      uint2 x[NU];
+#pragma unroll
+      for (int k = 0; k < NU; ++k) {
+        const int u = u0 + k * 64 * NWV;
+        if (u < kTile * UPR) {
+          const int r = u / UPR, c = u - r * UPR;
+          x[k] = *reinterpret_cast<const uint2*>(src + r * R + 8 * c);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NU; ++k) {
+        const int u = u0 + k * 64 * NWV;
+        if (u < kTile * UPR) {
+          const int r = u / UPR, c = u - r * UPR;
+          const uint4 y = {fp8x2_to_bf16x2<false>(x[k].x), fp8x2_to_bf16x2<true>(x[k].x),
+                           fp8x2_to_bf16x2<false>(x[k].y), fp8x2_to_bf16x2<true>(x[k].y)};
+          *reinterpret_cast<uint4*>(dst + lds_off<Cfg>(r, c)) = y;
+        }
       }
       // the tile's per-token scales, applied to its scores and to P (rows
       // past the sequence, masked, take row 0's finite scale)
-      if (threadIdx.x < kTile) scl[bslot * kTile + threadIdx.x] = tok0 + threadIdx.x < S ? sls[threadIdx.x] : sls[0];
+      if (u0 < kTile) scl[bslot * kTile + u0] = tok0 + u0 < S ? sls[u0] : sls[0];
     };
 
     if constexpr (Cfg::SPEC) {
@@ -1062,21 +1083,22 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // wait for tile it+1 -> barrier B (bf16 slot of tile it-1 and P(it) free /
     // visible) -> convert tile it+1 into the bf16 slot of tile it-1
     constexpr int SNB = Cfg::SNB;
+    const int ld8 = ld8_of(NW, wave);
 #pragma unroll
     for (int i = 0; i < SNB; ++i)
-      if (i < ntiles) issue_tile8(lt0 + i, i);
+      if (i < ntiles) issue_tile8(lt0 + i, i, std::integral_constant<int, NW>{}, wave);
     wait_vmcnt_le<2 * (Cfg::F8_BLK + 1)>(min(ntiles - 1, SNB - 1) * ld8);
     block_barrier();
-    convert8(lt0, 0, 0);
+    convert8(lt0, 0, 0, std::integral_constant<int, NW>{}, wave);
     for (int it = 0; it < ntiles; ++it) {
       block_barrier();
-      if (it + SNB < ntiles) issue_tile8(lt0 + it + SNB, it % SNB);
+      if (it + SNB < ntiles) issue_tile8(lt0 + it + SNB, it % SNB, std::integral_constant<int, NW>{}, wave);
       score_tile(lds + (it & 1) * Cfg::TILE_BYTES, (lt0 + it) * kTile, pass == 0 && it == 0, it & 1);
       if (it > 0) pv(lds + ((it - 1) & 1) * Cfg::TILE_BYTES, (it - 1) & 1);
       if (it + 1 < ntiles) {
         wait_vmcnt_le<2 * (Cfg::F8_BLK + 1)>((min(it + SNB, ntiles - 1) - (it + 1)) * ld8);
         block_barrier();
-        convert8(lt0 + it + 1, (it + 1) % SNB, (it + 1) & 1);
+        convert8(lt0 + it + 1, (it + 1) % SNB, (it + 1) & 1, std::integral_constant<int, NW>{}, wave);
       }
     }
     block_barrier();
