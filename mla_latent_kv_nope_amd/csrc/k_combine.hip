@@ -35,11 +35,12 @@ __device__ __forceinline__ PieceRange piece_range(const DecodeArgs& a, int b) {
 
 // Merged row chunks of head h of query sequence b: chunk k of this thread is
 // 8 columns starting at col[k]; acc[k] receives the merged fp32 values (not
-// yet rounded), the return value is the merged lse.  np >= 1.
-template <int CPT>
+// yet rounded), the return value is the merged lse.  np >= 1.  PG pieces'
+// chunks are in flight per round trip; the arithmetic (and so the result) is
+// the same for every PG.
+template <int CPT, int PG = 4>
 __device__ __forceinline__ float merge_chunks(const DecodeArgs& a, int b, PieceRange pr, int h,
                                               const int (&col)[CPT], float (&acc)[CPT][8]) {
-  constexpr int PG = 4;                              // pieces per round trip
   const int H = a.H, HP = (H + 15) & ~15;
   const int64_t slot0 = static_cast<int64_t>(pr.wf) + b;
   uint4 t[PG][CPT];
@@ -106,20 +107,21 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
 }
 
 // ---------------------------------------------------------------------------
-// k_combine: one workgroup per (query sequence, 16-head block); TPR threads
-// per head row, each merging CPT 16-byte chunks (a row's threads read
-// 16 * TPR contiguous bytes per chunk).  Writes o_lat / lse of split
-// sequences and o_lat = 0, lse = -inf for sequences with no tokens; a whole
-// sequence in one piece was written by k_split.
-template <int DC>
+// k_combine: one workgroup per (query sequence, RPW heads); TPR threads per
+// head row, each merging CPT 16-byte chunks (a row's threads read 16 * TPR
+// contiguous bytes per chunk), 16 / CPT pieces in flight (CPT 1: for batches
+// too small to fill the GPU with 16-head workgroups).  Writes o_lat / lse of
+// split sequences and o_lat = 0, lse = -inf for sequences with no tokens; a
+// whole sequence in one piece was written by k_split.
+template <int DC, int CPT>
 __global__ __launch_bounds__(64 * (DC / 128 > 0 ? DC / 128 : 1)) void k_combine(DecodeArgs a) {
   constexpr int THREADS = 64 * (DC / 128 > 0 ? DC / 128 : 1);
-  constexpr int TPR = THREADS / 16;
-  constexpr int CPT = DC / 8 / TPR;
-  static_assert(CPT * TPR * 8 == DC, "row split");
-  const int H = a.H, HG16 = (H + 15) >> 4;
-  const int b = blockIdx.x / HG16;
-  const int h = (blockIdx.x % HG16) * 16 + threadIdx.x / TPR;
+  constexpr int TPR = DC / 8 / CPT;
+  constexpr int RPW = THREADS / TPR;                 // head rows per workgroup
+  static_assert(CPT * TPR * 8 == DC && RPW * TPR == THREADS, "row split");
+  const int H = a.H, HGR = (H + RPW - 1) / RPW;
+  const int b = blockIdx.x / HGR;
+  const int h = (blockIdx.x % HGR) * RPW + threadIdx.x / TPR;
   if (h >= H) return;                                // (no barrier in this kernel)
   const int r = threadIdx.x % TPR;
   uint16_t* const orow = a.o_lat + (static_cast<int64_t>(b) * H + h) * DC;
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(64 * (DC / 128 > 0 ? DC / 128 : 1)) void k_combine(
 #pragma unroll
   for (int c = 0; c < CPT; ++c) col[c] = 8 * (r + TPR * c);
   float acc[CPT][8];
-  const float lse = merge_chunks<CPT>(a, b, pr, h, col, acc);
+  const float lse = merge_chunks<CPT, (16 / CPT < 4 ? 4 : 16 / CPT)>(a, b, pr, h, col, acc);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint4*>(orow + col[c]) = pack_bf16x8(acc[c]);
   if (a.lse != nullptr && r == 0) a.lse[static_cast<int64_t>(b) * H + h] = lse;
@@ -161,6 +163,48 @@ __global__ __launch_bounds__(64 * (DC / 128 > 0 ? DC / 128 : 1)) void k_combine(
 // blocks of one head share blockIdx mod 8, hence one XCD and its L2 copy of
 // W_UV[h].
 constexpr int kCpRows = 32;
+
+// Merge of rows row0 .. row0 + 8 CPT - 1 (query sequences) of head h into
+// bf16 o_lat rows in LDS (chunk j of row m at j ^ (m mod 16)), and to o_lat
+// / lse when asked: 64 / CPT threads per row, thread (m, r) taking chunks
+// r + (64 / CPT) k, k < CPT, with 16 / CPT pieces in flight.  Rows past the
+// batch (and sequences without tokens) are zero.
+template <int CPT>
+__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int h, int row0, char* ol) {
+  constexpr int DC = 512, TPR = 64 / CPT;
+  const int H = a.H, BQ = a.B;
+  const int m = threadIdx.x / TPR, r = threadIdx.x % TPR;
+  const int bq = row0 + m;
+  const PieceRange pr = bq < BQ ? piece_range(a, bq) : PieceRange{0, 0};
+  int col[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) col[c] = 8 * (r + TPR * c);
+  float acc[CPT][8];
+  float lse = -INFINITY;
+  if (pr.np > 0) {
+    lse = merge_chunks<CPT, 16 / CPT>(a, bq, pr, h, col, acc);
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+  }
+  uint4 pk[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    pk[c] = pack_bf16x8(acc[c]);
+    *reinterpret_cast<uint4*>(ol + m * (DC * 2) + 16 * ((r + TPR * c) ^ (m & 15))) = pk[c];
+  }
+  if (bq < BQ) {
+    if (a.o_lat != nullptr) {
+      uint16_t* const orow = a.o_lat + (static_cast<int64_t>(bq) * H + h) * DC;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint4*>(orow + col[c]) = pk[c];
+    }
+    if (a.lse != nullptr && r == 0) a.lse[static_cast<int64_t>(bq) * H + h] = lse;
+  }
+}
+
 __global__ __launch_bounds__(512) void k_combine_proj(DecodeArgs a, const uint16_t* w_uv, uint16_t* out) {
   constexpr int DC = 512, DV = 128, MR = kCpRows;
   constexpr int WROW = DV * 2;                       // bytes per W_UV row
@@ -174,11 +218,7 @@ __global__ __launch_bounds__(512) void k_combine_proj(DecodeArgs a, const uint16
   if (h >= H) return;                                // uniform per workgroup, before any barrier
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // ---- row, pieces, W_UV copy
-  const int m = threadIdx.x >> 4;                    // merge row of this thread
-  const int r = threadIdx.x & 15;
-  const int bq = rb * MR + m;
-  const PieceRange pr = bq < BQ ? piece_range(a, bq) : PieceRange{0, 0};
+  // ---- W_UV copy
   // copy i (0..127) fills LDS bytes [1024 i, +1024) = W rows 4i .. 4i + 3:
   // lane l fills row 4i + l/16 at chunk position l % 16 with logical chunk
   // (l % 16) ^ 2 (row mod 4); wave w issues copies 16w .. 16w + 15
@@ -193,36 +233,12 @@ __global__ __launch_bounds__(512) void k_combine_proj(DecodeArgs a, const uint16
     }
   }
 
-  // ---- merge: thread (m, r) takes chunks r + 16k, k = 0..3, of row m
-  {
-    int col[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) col[c] = 8 * (r + 16 * c);
-    float acc[4][8];
-    float lse = -INFINITY;
-    if (pr.np > 0) {
-      lse = merge_chunks<4>(a, bq, pr, h, col, acc);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-    }
-    uint4 pk[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      pk[c] = pack_bf16x8(acc[c]);
-      *reinterpret_cast<uint4*>(ol + m * (DC * 2) + 16 * ((r + 16 * c) ^ (m & 15))) = pk[c];
-    }
-    if (bq < BQ) {
-      if (a.o_lat != nullptr) {
-        uint16_t* const orow = a.o_lat + (static_cast<int64_t>(bq) * H + h) * DC;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(orow + col[c]) = pk[c];
-      }
-      if (a.lse != nullptr && r == 0) a.lse[static_cast<int64_t>(bq) * H + h] = lse;
-    }
-  }
+  // ---- merge: with few rows in the block, each row is spread over more
+  // threads (fewer chunks each) and more pieces are in flight per round trip
+  const int nrows = min(MR, BQ - rb * MR);
+  if (nrows <= 8) merge_rows<1>(a, h, rb * MR, ol);
+  else if (nrows <= 16) merge_rows<2>(a, h, rb * MR, ol);
+  else merge_rows<4>(a, h, rb * MR, ol);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -261,13 +277,18 @@ __global__ __launch_bounds__(512) void k_combine_proj(DecodeArgs a, const uint16
 }  // namespace
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
-  const int hg16 = (a.H + 15) / 16;
-  if (a.d_c == 512)
-    hipLaunchKernelGGL(k_combine<512>, dim3(a.B * hg16), dim3(256), 0, s, a);
-  else if (a.d_c == 32)
-    hipLaunchKernelGGL(k_combine<32>, dim3(a.B * hg16), dim3(64), 0, s, a);
-  else
+  const int64_t hg16 = (a.H + 15) / 16, hg4 = (a.H + 3) / 4;
+  if (a.d_c == 512) {
+    // 16 heads per workgroup while that fills the compute units; else 4
+    if (a.B * hg16 >= 256)
+      hipLaunchKernelGGL((k_combine<512, 4>), dim3(static_cast<unsigned>(a.B * hg16)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_combine<512, 1>), dim3(static_cast<unsigned>(a.B * hg4)), dim3(256), 0, s, a);
+  } else if (a.d_c == 32) {
+    hipLaunchKernelGGL((k_combine<32, 1>), dim3(static_cast<unsigned>(a.B * hg16)), dim3(64), 0, s, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
