@@ -2,7 +2,8 @@
 """Benchmark of one MLA absorbed-decode step on one MI355X.
 
 A step is the whole hot path for one new token per sequence:
-  mla_append_latent (the B new rows) -> mla_absorb_q -> mla_decode_paged_out
+  mla_append_absorb (mla_append_latent of the B new rows and mla_absorb_q in
+  one launch) -> mla_decode_paged_out
   (split attention with its own tile plan, then the LSE merge and the W_UV
   output projection in one kernel),
 on the DeepSeek-V3-shaped workload (B=64, H=128, d_c=512, d_rope=64,
@@ -446,11 +447,12 @@ def main():
                                    t["seq_lens"], args.num_splits, ws, o_lat.view(B, ql, H, wl.d_c),
                                    lse.view(B, ql, H), events=ev)
 
-    # the step: decode with the W_UV projection in its merge kernel (o_lat and
-    # lse are not needed downstream and are not written)
+    # the step: the append and the query absorption in one launch, then decode
+    # with the W_UV projection in its merge kernel (o_lat and lse are not
+    # needed downstream and are not written)
     def step(ev=None):
-        mla.append_latent(d, new_c, new_k, new_pos, new_sid, t["block_table"], pool, scales)
-        mla.absorb_q(d, q_nope, q_pe, q_pos, t["w_uk"], q)
+        mla.append_absorb(d, new_c, new_k, new_pos, new_sid, t["block_table"], pool, scales,
+                          q_nope, q_pe, q_pos, t["w_uk"], q)
         mla.decode_paged_out(d, q.view(B, ql, H, R), pool, scales, t["block_table"], t["seq_lens"],
                              t["w_uv"], args.num_splits, ws, out.view(B, ql, H, wl.d_v), events=ev)
 
@@ -528,8 +530,8 @@ def main():
                    "total_tokens": total_tokens,
                    "page_size": wl.page_size, "cache": "fp8_e4m3" if wl.fp8 else "bf16",
                    "num_splits": args.num_splits or "auto",
-                   "step": ("append+absorb+decode_out(plan,split,merge+W_UV projection)" if ql == 1 else
-                            f"append({ql} new tokens per sequence)+absorb+decode_out(plan,split,"
+                   "step": ("append_absorb+decode_out(plan,split,merge+W_UV projection)" if ql == 1 else
+                            f"append_absorb({ql} new tokens per sequence)+decode_out(plan,split,"
                             f"merge+W_UV projection); value counts the B*q_len new tokens scored")},
         "decode_kernel_tokens_per_s": round(BQ / (split_ms * 1e-3), 1),
         "launch": "hip graph replay of the captured step" if args.graph else "eager calls",

@@ -229,6 +229,30 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void
                           void* stream);
 
 /*
+ * mla_append_absorb - mla_append_latent and mla_absorb_q of one decode step in
+ * a single launch: the append's workgroups (one wave per new token) run after
+ * the absorption's, in its tail, instead of as a kernel of their own.
+ * Source: the step appends the new latent rows before attending
+ * (sheratonhq.com section 2.1) and absorbs W_UK into the query (same section;
+ * zskr.cn sections 2.2 and 4.2, the fused Q x W_DK kernel); kernel fusion
+ * against launch and memory round trips (zskr.cn section 4.2).
+ *
+ * Arguments c_kv .. flags as for mla_append_latent, q_nope .. q_out as for
+ * mla_absorb_q; both sets are checked as those calls check them (the first
+ * failing check's status is returned, nothing is enqueued then).  Results are
+ * those of mla_append_latent followed by mla_absorb_q: the two write disjoint
+ * memory (pool rows and scales; q_out) and read nothing the other writes, so
+ * their order does not matter.  n_tokens = 0 only absorbs.
+ */
+mla_status_t mla_append_absorb(const mla_dims_t* dims, const void* c_kv, const void* k_pe,
+                               const int32_t* positions, const int32_t* seq_ids,
+                               const int32_t* block_table, int32_t num_seqs, int32_t max_pages,
+                               int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
+                               uint32_t flags, const void* q_nope, const void* q_pe,
+                               const int32_t* q_pos, const void* w_uk, int32_t B, void* q_out,
+                               void* stream);
+
+/*
  * mla_decode_workspace_size - bytes of device workspace mla_decode_paged needs
  * for this batch size and split count (num_splits as in mla_decode_paged).
  * Returns 0 for unsupported dims or B <= 0.

@@ -6,7 +6,7 @@ first use of any binding attribute, and that use fails (ImportError) if the
 library is missing; `mla_latent_kv_nope_amd.build` builds it.
 """
 _API = (
-    "Dims", "LIB_PATH", "MlaError", "absorb_q", "append_latent", "cache_bytes_per_token",
+    "Dims", "LIB_PATH", "MlaError", "absorb_q", "append_absorb", "append_latent", "cache_bytes_per_token",
     "decode_paged", "decode_paged_multi", "decode_paged_noalloc", "decode_noalloc_max_bytes",
     "decode_paged_out",
     "decode_workspace_size", "make_dims", "new_pool",

@@ -51,7 +51,7 @@ EXPORTS = (
     "mla_out_proj", "mla_cache_bytes_per_token", "mla_status_string", "mla_last_hip_error",
     "mla_decode_paged_timed", "mla_prefill_paged_timed", "mla_decode_paged_noalloc",
     "mla_decode_noalloc_max_bytes", "mla_prefill_workspace_size", "mla_prefill_paged",
-    "mla_decode_paged_out",
+    "mla_decode_paged_out", "mla_append_absorb",
 )
 
 _P = ctypes.c_void_p
@@ -70,6 +70,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_append_latent.restype = ctypes.c_int
     lib.mla_absorb_q.argtypes = [_DP, _P, _P, _P, _P, _I, _P, _P]
     lib.mla_absorb_q.restype = ctypes.c_int
+    lib.mla_append_absorb.argtypes = [_DP, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_uint32,
+                                      _P, _P, _P, _P, _I, _P, _P]
+    lib.mla_append_absorb.restype = ctypes.c_int
     lib.mla_decode_workspace_size.argtypes = [_DP, _I, _I]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_paged.argtypes = [_DP, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, ctypes.c_size_t,

@@ -180,6 +180,49 @@ def absorb_q(d: Dims, q_nope: torch.Tensor, q_pe: torch.Tensor, q_pos: torch.Ten
     return q_out
 
 
+def append_absorb(d: Dims, c_kv: torch.Tensor, k_pe: torch.Tensor, positions: torch.Tensor,
+                  seq_ids: torch.Tensor, block_table: torch.Tensor, pool: torch.Tensor,
+                  scales: Optional[torch.Tensor], q_nope: torch.Tensor, q_pe: torch.Tensor,
+                  q_pos: torch.Tensor, w_uk: torch.Tensor, q_out: Optional[torch.Tensor] = None,
+                  rope: bool = True) -> torch.Tensor:
+    """mla_append_absorb: append_latent(c_kv, k_pe, ...) and absorb_q(q_nope,
+    q_pe, q_pos, w_uk) in one launch; returns q_out."""
+    T = c_kv.shape[0]
+    _req(c_kv, "c_kv", torch.bfloat16, (T, d.d_c))
+    _req(k_pe, "k_pe", torch.bfloat16, (T, d.d_rope))
+    _req(positions, "positions", torch.int32, (T,))
+    _req(seq_ids, "seq_ids", torch.int32, (T,))
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs][max_pages]")
+    _req(block_table, "block_table", torch.int32)
+    num_pages = pool.shape[0]
+    if _is_fp8(d):
+        _req(pool, "pool", torch.uint8, pool_shape(d, num_pages))
+        if scales is None:
+            raise ValueError("an fp8 cache needs its scales tensor")
+        _req(scales, "scales", torch.float32, (num_pages, d.page_size))
+    else:
+        _req(pool, "pool", torch.bfloat16, pool_shape(d, num_pages))
+        if scales is not None:
+            raise ValueError("a bf16 cache has no scales")
+    B = q_nope.shape[0]
+    H = d.n_heads
+    _req(q_nope, "q_nope", torch.bfloat16, (B, H, d.d_nope))
+    _req(q_pe, "q_pe", torch.bfloat16, (B, H, d.d_rope))
+    _req(q_pos, "q_pos", torch.int32, (B,))
+    _req(w_uk, "w_uk", torch.bfloat16, (H, d.d_c, d.d_nope))
+    if q_out is None:
+        q_out = torch.empty((B, H, d.d_c + d.d_rope), dtype=torch.bfloat16, device=q_nope.device)
+    _req(q_out, "q_out", torch.bfloat16, (B, H, d.d_c + d.d_rope))
+    st = lib.mla_append_absorb(
+        ctypes.byref(d), _ptr(c_kv), _ptr(k_pe), _ptr(positions), _ptr(seq_ids), _ptr(block_table),
+        block_table.shape[0], block_table.shape[1], num_pages, T, _ptr(pool), _ptr(scales),
+        0 if rope else _native.MLA_APPEND_NO_ROPE, _ptr(q_nope), _ptr(q_pe), _ptr(q_pos), _ptr(w_uk), B,
+        _ptr(q_out), _stream())
+    _check("mla_append_absorb", st)
+    return q_out
+
+
 def decode_workspace_size(d: Dims, B: int, num_splits: int = 0) -> int:
     n = lib.mla_decode_workspace_size(ctypes.byref(d), int(B), int(num_splits))
     if n == 0:

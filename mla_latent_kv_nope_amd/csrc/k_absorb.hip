@@ -9,6 +9,7 @@
 // A per-head batched GEMM [B x d_nope] x [d_nope x d_c] on 32x32x16 bf16 MFMA.
 // Both operands are contiguous along the reduction axis (q_nope rows, W_UK
 // rows), so they are loaded straight into MFMA registers.
+#include "append.hpp"
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -43,7 +44,7 @@ __device__ __forceinline__ void rope_rotate(float x0, float x1, double s, double
 // evaluated in fp64.  Every workgroup needs 40 KB of LDS, so four fit on a CU
 // and a 64-row batch at 128 heads runs in a single round of 1024 workgroups.
 template <int DC, int DN>
-__global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
+__device__ __forceinline__ void absorb_block(const AbsorbArgs& a, int bid) {
   constexpr int COLS = DC < 128 ? DC : 128;  // latent columns per workgroup
   constexpr int NCB = DC / COLS;             // column blocks per head
   static_assert(COLS % 32 == 0 && DN % 16 == 0 && 32 % NCB == 0, "tile shape");
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
   __shared__ __attribute__((aligned(1024))) char wl[WL_BYTES > OL_BYTES ? WL_BYTES : OL_BYTES];
   __shared__ __attribute__((aligned(1024))) char ql[32 * ROWB];     // q_nope rows [32][DN]
   uint16_t* const ol = reinterpret_cast<uint16_t*>(wl);
-  int id = blockIdx.x;
+  int id = bid;
   const int cbk = id % NCB;
   id /= NCB;
   const int h = id % H;
@@ -157,10 +158,49 @@ __global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
   }
 }
 
+template <int DC, int DN>
+__global__ __launch_bounds__(256) void k_absorb(AbsorbArgs a) {
+  absorb_block<DC, DN>(a, blockIdx.x);
+}
+
+// The absorb workgroups, then ceil(n_tokens / 4) workgroups that append the
+// step's new latent rows (one wave per token).  The two parts touch disjoint
+// memory; the append workgroups come last, so they run in the absorb's tail
+// instead of holding back absorb workgroups.
+template <int DC, int DN, bool FP8>
+__global__ __launch_bounds__(256) void k_absorb_append(AbsorbArgs a, AppendArgs p, int n_absorb) {
+  const int bid = blockIdx.x;
+  if (bid >= n_absorb) {
+    append_token<FP8, false>(p, (bid - n_absorb) * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+    return;
+  }
+  absorb_block<DC, DN>(a, bid);
+}
+
 }  // namespace
 
 bool absorb_supported(int d_c, int d_nope) {
   return (d_c == 512 && d_nope == 128) || (d_c == 32 && d_nope == 16);
+}
+
+hipError_t launch_absorb_append(const AbsorbArgs& a, const AppendArgs& p, hipStream_t s) {
+  const dim3 block(256);
+  const int rb = (a.B + 31) / 32;
+  if (a.d_rope / 2 * (32 / (a.d_c < 128 ? 1 : a.d_c / 128)) > 256) return hipErrorInvalidValue;
+  if (p.part != nullptr) return hipErrorInvalidValue;
+  const int n_app = (p.n_tokens + 3) / 4;
+  if (a.d_c == 512 && a.d_nope == 128) {
+    const int n_abs = a.H * 4 * rb;
+    if (p.fp8) hipLaunchKernelGGL((k_absorb_append<512, 128, true>), dim3(n_abs + n_app), block, 0, s, a, p, n_abs);
+    else hipLaunchKernelGGL((k_absorb_append<512, 128, false>), dim3(n_abs + n_app), block, 0, s, a, p, n_abs);
+  } else if (a.d_c == 32 && a.d_nope == 16) {
+    const int n_abs = a.H * rb;
+    if (p.fp8) hipLaunchKernelGGL((k_absorb_append<32, 16, true>), dim3(n_abs + n_app), block, 0, s, a, p, n_abs);
+    else hipLaunchKernelGGL((k_absorb_append<32, 16, false>), dim3(n_abs + n_app), block, 0, s, a, p, n_abs);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s) {

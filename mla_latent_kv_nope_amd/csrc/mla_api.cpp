@@ -78,41 +78,109 @@ size_t mla_cache_bytes_per_token(const mla_dims_t* d) {
   return 0;
 }
 
-mla_status_t mla_append_latent(const mla_dims_t* d, const void* c_kv, const void* k_pe,
-                               const int32_t* positions, const int32_t* seq_ids,
-                               const int32_t* block_table, int32_t num_seqs, int32_t max_pages,
-                               int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
-                               uint32_t flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks and kernel arguments of mla_append_latent; *empty is set
+// when there is nothing to append (then `a` is not filled).
+mla_status_t append_args(const mla_dims_t* d, const void* c_kv, const void* k_pe, const int32_t* positions,
+                         const int32_t* seq_ids, const int32_t* block_table, int32_t num_seqs,
+                         int32_t max_pages, int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
+                         uint32_t flags, mla::AppendArgs* a, bool* empty) {
   const mla_status_t st = check_dims(d);
   if (st != MLA_OK) return st;
   if (n_tokens < 0 || num_seqs <= 0 || max_pages <= 0 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
   if ((flags & ~MLA_APPEND_NO_ROPE) != 0) return MLA_ERR_INVALID_ARG;
-  if (n_tokens == 0) return MLA_OK;
+  *empty = n_tokens == 0;
+  if (*empty) return MLA_OK;
   if (!c_kv || !k_pe || !positions || !seq_ids || !block_table || !pool) return MLA_ERR_INVALID_ARG;
   const bool fp8 = d->cache_dtype == MLA_CACHE_FP8_E4M3;
   if (fp8 != (scales != nullptr)) return MLA_ERR_INVALID_ARG;
   if (!aligned(c_kv, 16) || !aligned(k_pe, 4) || !aligned(pool, 16) || !aligned(positions, 4) ||
       !aligned(seq_ids, 4) || !aligned(block_table, 4) || (fp8 && !aligned(scales, 4)))
     return MLA_ERR_INVALID_ARG;
-  mla::AppendArgs a{};
-  a.d_c = d->d_c;
-  a.d_rope = d->d_rope;
-  a.page_size_log2 = log2_exact(d->page_size);
-  a.max_pages = max_pages;
-  a.num_pages = num_pages;
-  a.num_seqs = num_seqs;
-  a.n_tokens = n_tokens;
-  a.fp8 = fp8;
-  a.rope = (flags & MLA_APPEND_NO_ROPE) == 0;
-  a.rope_base = d->rope_base;
-  a.c_kv = static_cast<const uint16_t*>(c_kv);
-  a.k_pe = static_cast<const uint16_t*>(k_pe);
-  a.positions = positions;
-  a.seq_ids = seq_ids;
-  a.block_table = block_table;
-  a.pool = pool;
-  a.scales = scales;
+  *a = mla::AppendArgs{};
+  a->d_c = d->d_c;
+  a->d_rope = d->d_rope;
+  a->page_size_log2 = log2_exact(d->page_size);
+  a->max_pages = max_pages;
+  a->num_pages = num_pages;
+  a->num_seqs = num_seqs;
+  a->n_tokens = n_tokens;
+  a->fp8 = fp8;
+  a->rope = (flags & MLA_APPEND_NO_ROPE) == 0;
+  a->rope_base = d->rope_base;
+  a->c_kv = static_cast<const uint16_t*>(c_kv);
+  a->k_pe = static_cast<const uint16_t*>(k_pe);
+  a->positions = positions;
+  a->seq_ids = seq_ids;
+  a->block_table = block_table;
+  a->pool = pool;
+  a->scales = scales;
+  return MLA_OK;
+}
+
+// Argument checks and kernel arguments of mla_absorb_q.
+mla_status_t absorb_args(const mla_dims_t* d, const void* q_nope, const void* q_pe, const int32_t* q_pos,
+                         const void* w_uk, int32_t B, void* q_out, mla::AbsorbArgs* a) {
+  const mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (B <= 0) return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !q_pe || !q_pos || !w_uk || !q_out) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 4) || !aligned(q_pos, 4) || !aligned(w_uk, 16) ||
+      !aligned(q_out, 16))
+    return MLA_ERR_INVALID_ARG;
+  if (!mla::absorb_supported(d->d_c, d->d_nope)) return MLA_ERR_UNSUPPORTED;
+  *a = mla::AbsorbArgs{};
+  a->B = B;
+  a->H = d->n_heads;
+  a->d_c = d->d_c;
+  a->d_rope = d->d_rope;
+  a->d_nope = d->d_nope;
+  a->rope_base = d->rope_base;
+  a->q_nope = static_cast<const uint16_t*>(q_nope);
+  a->q_pe = static_cast<const uint16_t*>(q_pe);
+  a->q_pos = q_pos;
+  a->w_uk = static_cast<const uint16_t*>(w_uk);
+  a->q_out = static_cast<uint16_t*>(q_out);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_append_latent(const mla_dims_t* d, const void* c_kv, const void* k_pe,
+                               const int32_t* positions, const int32_t* seq_ids,
+                               const int32_t* block_table, int32_t num_seqs, int32_t max_pages,
+                               int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
+                               uint32_t flags, void* stream) {
+  mla::AppendArgs a;
+  bool empty = false;
+  const mla_status_t st = append_args(d, c_kv, k_pe, positions, seq_ids, block_table, num_seqs, max_pages,
+                                      num_pages, n_tokens, pool, scales, flags, &a, &empty);
+  if (st != MLA_OK || empty) return st;
   return from_hip(mla::launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_append_absorb(const mla_dims_t* d, const void* c_kv, const void* k_pe,
+                               const int32_t* positions, const int32_t* seq_ids,
+                               const int32_t* block_table, int32_t num_seqs, int32_t max_pages,
+                               int32_t num_pages, int32_t n_tokens, void* pool, float* scales,
+                               uint32_t flags, const void* q_nope, const void* q_pe, const int32_t* q_pos,
+                               const void* w_uk, int32_t B, void* q_out, void* stream) {
+  mla::AppendArgs p;
+  bool empty = false;
+  mla_status_t st = append_args(d, c_kv, k_pe, positions, seq_ids, block_table, num_seqs, max_pages,
+                                num_pages, n_tokens, pool, scales, flags, &p, &empty);
+  if (st != MLA_OK) return st;
+  mla::AbsorbArgs a;
+  st = absorb_args(d, q_nope, q_pe, q_pos, w_uk, B, q_out, &a);
+  if (st != MLA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (empty) return from_hip(mla::launch_absorb(a, s));
+  return from_hip(mla::launch_absorb_append(a, p, s));
 }
 
 namespace {
@@ -185,26 +253,9 @@ mla_status_t mla_project_append(const mla_dims_t* d, int32_t d_model, const void
 mla_status_t mla_absorb_q(const mla_dims_t* d, const void* q_nope, const void* q_pe,
                           const int32_t* q_pos, const void* w_uk, int32_t B, void* q_out,
                           void* stream) {
-  const mla_status_t st = check_dims(d);
+  mla::AbsorbArgs a;
+  const mla_status_t st = absorb_args(d, q_nope, q_pe, q_pos, w_uk, B, q_out, &a);
   if (st != MLA_OK) return st;
-  if (B <= 0) return MLA_ERR_INVALID_ARG;
-  if (!q_nope || !q_pe || !q_pos || !w_uk || !q_out) return MLA_ERR_INVALID_ARG;
-  if (!aligned(q_nope, 16) || !aligned(q_pe, 4) || !aligned(q_pos, 4) || !aligned(w_uk, 16) ||
-      !aligned(q_out, 16))
-    return MLA_ERR_INVALID_ARG;
-  if (!mla::absorb_supported(d->d_c, d->d_nope)) return MLA_ERR_UNSUPPORTED;
-  mla::AbsorbArgs a{};
-  a.B = B;
-  a.H = d->n_heads;
-  a.d_c = d->d_c;
-  a.d_rope = d->d_rope;
-  a.d_nope = d->d_nope;
-  a.rope_base = d->rope_base;
-  a.q_nope = static_cast<const uint16_t*>(q_nope);
-  a.q_pe = static_cast<const uint16_t*>(q_pe);
-  a.q_pos = q_pos;
-  a.w_uk = static_cast<const uint16_t*>(w_uk);
-  a.q_out = static_cast<uint16_t*>(q_out);
   return from_hip(mla::launch_absorb(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -105,6 +105,9 @@ int decode_auto_parts(int B, int H);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_down(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_absorb(const AbsorbArgs& a, hipStream_t s);
+// launch_absorb and launch_append (bf16 / fp8 rows from c_kv and k_pe, not
+// from partial sums) as one launch
+hipError_t launch_absorb_append(const AbsorbArgs& a, const AppendArgs& p, hipStream_t s);
 hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t s);
 // split kernel (with its plan); `ev0`/`ev1` (may be null) are recorded
 // immediately before and after it.  With a.o_lat null every piece, a whole

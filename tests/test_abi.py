@@ -213,6 +213,28 @@ def test_decode_out_validation():
     _expect(call(dims=tiny, wsb=1 << 30), _native.MLA_ERR_UNSUPPORTED)
 
 
+def test_append_absorb_validation():
+    """mla_append_absorb checks both argument sets as the separate calls do."""
+    d = mla.make_dims(128, 512, 64, 128, 128, 64)
+    f = lib.mla_append_absorb
+
+    def call(c_kv=P, T=5, flags=0, q_nope=P, B=4, w_uk=P, scales=None, dims=d, q_out=P):
+        return f(ctypes.byref(dims), c_kv, P, P, P, P, 4, 8, 40, T, P, scales, flags,
+                 q_nope, P, P, w_uk, B, q_out, None)
+
+    _expect(call(c_kv=None), _native.MLA_ERR_INVALID_ARG)        # append side
+    _expect(call(c_kv=P + 2), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(T=-1), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(flags=7), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(scales=P), _native.MLA_ERR_INVALID_ARG)         # scales with a bf16 cache
+    _expect(call(q_nope=None), _native.MLA_ERR_INVALID_ARG)      # absorb side
+    _expect(call(B=0), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(w_uk=P + 8), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(q_out=None), _native.MLA_ERR_INVALID_ARG)
+    _expect(call(T=0, B=0), _native.MLA_ERR_INVALID_ARG)         # nothing to append, still absorbs
+    _expect(call(dims=mla.make_dims(129, 512, 64, 128, 128, 64)), _native.MLA_ERR_UNSUPPORTED)
+
+
 def test_binding_rejects_host_tensors():
     import torch
     d = mla.make_dims(4, 32, 16, 16, 16, 16)

@@ -24,7 +24,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["decode+out_proj", "decode_out"])
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_calls", "append_absorb+decode_out"])
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
 def test_captured_step_replays_bit_for_bit(wl, fused):
     inp = make_inputs(wl)
@@ -51,9 +51,13 @@ def test_captured_step_replays_bit_for_bit(wl, fused):
     q_nope = t["q_nope"].clone()
 
     def step():
-        mla.append_latent(d, new["c_kv"], new["k_pe"], new["positions"], new["seq_ids"],
-                          t["block_table"], pool, scales)
-        mla.absorb_q(d, q_nope, t["q_pe"], t["q_pos"], t["w_uk"], q)
+        if fused:
+            mla.append_absorb(d, new["c_kv"], new["k_pe"], new["positions"], new["seq_ids"],
+                              t["block_table"], pool, scales, q_nope, t["q_pe"], t["q_pos"], t["w_uk"], q)
+        else:
+            mla.append_latent(d, new["c_kv"], new["k_pe"], new["positions"], new["seq_ids"],
+                              t["block_table"], pool, scales)
+            mla.absorb_q(d, q_nope, t["q_pe"], t["q_pos"], t["w_uk"], q)
         if fused:
             mla.decode_paged_out(d, q, pool, scales, t["block_table"], t["seq_lens"], t["w_uv"], 0, ws,
                                  out, o_lat, lse)
