@@ -139,6 +139,7 @@ def bench_project_append(args):
     sid = torch.arange(B, dtype=torch.int32, device=dev)
     ws = torch.empty(mla.project_append_workspace_size(d, d_model, B), dtype=torch.uint8, device=dev)
     call = lambda: mla.project_append(d, h, w, pos, sid, bt, pool, None, ws)
+    settled = settle(torch, call)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -154,7 +155,7 @@ def bench_project_append(args):
     gbs = nbytes / (us * 1e-6) / 1e9
     print(json.dumps({
         "metric": "mla_project_append time per decode step (64 new tokens)", "value": round(us, 3),
-        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle": settled,
         "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "V3 decode step's new tokens: T=64, d_model=7168 -> 576-wide rows, "
                                "page 64, permuted pages", "tokens": B, "d_model": d_model,
@@ -198,6 +199,7 @@ def bench_prefill(args):
     lse = torch.empty((B * n, H), dtype=torch.float32, device=dev)
     call = lambda ev=None: mla.prefill_paged(d, qn, qp, q_start, n, pool, None, t["block_table"],
                                              t["seq_lens"], t["w_uk"], t["w_uv"], ws, out, lse, events=ev)
+    settled = settle(torch, call)
     for _ in range(args.warmup):
         call()
     evs = kernel_events(torch, args.steps)
@@ -219,7 +221,7 @@ def bench_prefill(args):
         "metric": "MLA explicit-form prefill tokens/s (chunk of 4096 new tokens on 8192-token "
                   "sequences, H=128)",
         "value": round(B * n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle": settled, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "V3 prefill chunk: B=2, S=8192, 4096 new tokens each (the second "
@@ -237,6 +239,29 @@ def bench_prefill(args):
     if args.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline_prefill(inp)
     print(json.dumps(line), flush=True)
+
+
+# GPU time the step runs untimed before the counted warm-up steps.  From idle
+# the GPU needs tens of milliseconds of load to reach its steady clocks:
+# measured, 20 timed V3 steps after 5 warm-up steps took 176 us per split
+# launch, after 200 warm-up steps (about 38 ms) 152 us.
+SETTLE_MS = 100.0
+
+
+def settle(torch, fn, min_ms: float = SETTLE_MS) -> dict:
+    """Runs fn() untimed until at least min_ms of wall time have passed (the
+    GPU kept busy: a synchronise every 20 calls), then synchronises."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(20):
+            fn()
+        n += 20
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            break
+    return {"calls": n, "ms": round((time.perf_counter() - t0) * 1e3, 1),
+            "why": "untimed, before the warm-up steps: the GPU leaves its idle clock state"}
 
 
 def kernel_events(torch, n: int):
@@ -456,6 +481,7 @@ def main():
         mla.decode_paged_out(d, q.view(B, ql, H, R), pool, scales, t["block_table"], t["seq_lens"],
                              t["w_uv"], args.num_splits, ws, out.view(B, ql, H, wl.d_v), events=ev)
 
+    settled = settle(torch, step)
     for _ in range(args.warmup):
         step()
     evs = kernel_events(torch, args.steps)
@@ -535,6 +561,7 @@ def main():
                             f"merge+W_UV projection); value counts the B*q_len new tokens scored")},
         "decode_kernel_tokens_per_s": round(BQ / (split_ms * 1e-3), 1),
         "launch": "hip graph replay of the captured step" if args.graph else "eager calls",
+        "settle": settled,
         "roofline": roof,
     }
     if args.graph:
