@@ -20,9 +20,10 @@
 //              pool straight into MFMA registers in four quarters of the
 //              reduction, the next quarter loading while this quarter's
 //              MFMAs run; an fp8 cache's codes become bf16 (code * scale) at
-//              the MFMA.  K_nope is written [t][h][128], V transposed
-//              [h][128][t] (the MFMA operands are swapped for V, so both
-//              stores are 64-byte runs); the head-0 workgroups of the K launch
+//              the MFMA.  K_nope is written [h][t][128] and V transposed
+//              per 32-token tile, [h][t / 32][128][32] (the MFMA operands are
+//              swapped for V), so a key tile of one head is one contiguous
+//              8 KB run in each; the head-0 workgroups of the K launch
 //              also write the shared RoPE keys [t][64] as bf16.
 //   k_prefill  one workgroup of four waves per (sequence, head, 128 new
 //              tokens); each wave owns 32 queries.  K_nope, RoPE-key and V^T
@@ -231,12 +232,12 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
         // uniform
         // (the stride is made opaque here so that its 64 multiples are formed
         // at the stores in scalar registers, not hoisted out of the loop)
-        int64_t ts = static_cast<int64_t>(a.H) * kPfDh;                // token stride
+        int64_t ts = kPfDh;                                             // token stride
         __asm__ volatile("" : "+s"(ts));
         // lanes 2m and 2m + 1 swap one value (a 2 x 2 transpose), so each
         // stores two adjacent columns of one token as one 4-byte word: the
         // even lane token 8 (i/4) + i%4, the odd lane the next token
-        uint16_t* kb = a.kn + ((static_cast<int64_t>(b) * a.s_pad + tblk) * a.H + h) * kPfDh +
+        uint16_t* kb = a.kn + ((static_cast<int64_t>(b) * a.H + h) * a.s_pad + tblk) * kPfDh +
                        4 * half * ts + (r & ~1);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
@@ -250,12 +251,12 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
         // the address is in the base pointer, the rest is uniform
         // (the stride is made opaque here so that its 64 multiples are formed
         // at the stores in scalar registers, not hoisted out of the loop)
-        int64_t cs = a.s_pad;                                           // column stride
+        int64_t cs = kPfKTile;                                          // column stride
         __asm__ volatile("" : "+s"(cs));
         // lanes 2m and 2m + 1 hold adjacent slots; after the 2 x 2 transpose
         // each stores both slots of one column as one 4-byte word: the even
         // lane column 32 ct + 8 (i/4) + 4 half + i%4, the odd lane the next
-        uint16_t* vb = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * cs + tblk +
+        uint16_t* vb = a.vt + ((static_cast<int64_t>(b) * a.H + h) * a.s_pad + tblk) * kPfDh +
                        4 * half * cs + vt_slot(r & ~1);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
@@ -366,8 +367,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
   }
 
   const uint16_t* kr_b = a.kr + static_cast<int64_t>(b) * a.s_pad * kPfDr;
-  const uint16_t* kn_b = a.kn + static_cast<int64_t>(b) * a.s_pad * a.H * kPfDh;
-  const uint16_t* vt_bh = a.vt + (static_cast<int64_t>(b) * a.H + h) * kPfDh * a.s_pad;
+  const uint16_t* kn_bh = a.kn + (static_cast<int64_t>(b) * a.H + h) * a.s_pad * kPfDh;
+  const uint16_t* vt_bh = a.vt + (static_cast<int64_t>(b) * a.H + h) * a.s_pad * kPfDh;
   // copies of key tile nt into slot base: 8 K_nope, 4 K_rope and 8 V^T copies
   // of 1 KB, five per wave; lane l of a copy fills LDS bytes [16 l, +16).
   // Each lane's sources for tile 0 are formed once; tile nt adds a uniform
@@ -378,9 +379,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
   for (int k2 = 0; k2 < 2; ++k2) {
     const int k = wave + 4 * k2;
     const int kr = 4 * k + (lane >> 4);
-    src_kn[k2] = kn_b + (static_cast<int64_t>(kr) * a.H + h) * kPfDh + 8 * ((lane & 15) ^ (kr & 15));
+    src_kn[k2] = kn_bh + kr * kPfDh + 8 * ((lane & 15) ^ (kr & 15));
     const int j = 16 * k + (lane >> 2);
-    src_vt[k2] = vt_bh + static_cast<int64_t>(j) * a.s_pad + 8 * ((lane & 3) ^ ((j >> 2) & 3));
+    src_vt[k2] = vt_bh + j * kPfKTile + 8 * ((lane & 3) ^ ((j >> 2) & 3));
   }
   const uint16_t* src_kr;
   {
@@ -391,11 +392,11 @@ __global__ __launch_bounds__(256, 2) void k_prefill(PrefillArgs a) {
     const int64_t t0 = static_cast<int64_t>(kPfKTile) * nt;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
-      lds_dma16_v(src_kn[k2] + t0 * a.H * kPfDh, lds_addr(base + kSlotKn + 1024 * (wave + 4 * k2)));
+      lds_dma16_v(src_kn[k2] + t0 * kPfDh, lds_addr(base + kSlotKn + 1024 * (wave + 4 * k2)));
     lds_dma16_v(src_kr + t0 * kPfDr, lds_addr(base + kSlotKr + 1024 * wave));
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
-      lds_dma16_v(src_vt[k2] + t0, lds_addr(base + kSlotVt + 1024 * (wave + 4 * k2)));
+      lds_dma16_v(src_vt[k2] + t0 * kPfDh, lds_addr(base + kSlotVt + 1024 * (wave + 4 * k2)));
   };
 
   float m = kNegInf, l = 0.f;

@@ -34,8 +34,8 @@ struct PrefillArgs {
   const int32_t* seq_lens;     // [B]
   const uint16_t* w_uk;        // [H][512][128]
   const uint16_t* w_uv;        // [H][512][128]
-  uint16_t* kn;                // workspace [B][s_pad][H][128]: K_nope = C . W_UK[h]
-  uint16_t* vt;                // workspace [B][H][128][s_pad]: V^T, V = C . W_UV[h]
+  uint16_t* kn;                // workspace [B][H][s_pad][128]: K_nope = C . W_UK[h]
+  uint16_t* vt;                // workspace [B][H][s_pad / 32][128][32]: V^T per 32-token tile, V = C . W_UV[h]
   uint16_t* kr;                // workspace [B][s_pad][64]: the rotated RoPE keys, bf16
   uint16_t* out;               // [T][H][128]
   float* lse;                  // [T][H] or nullptr
