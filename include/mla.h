@@ -136,8 +136,9 @@ mla_status_t mla_append_latent(const mla_dims_t* dims, const void* c_kv, const v
  *   workspace   device buffer of at least mla_project_append_workspace_size()
  *               bytes, 256-byte aligned (fp32 partial sums; no initialisation)
  *   other arguments as for mla_append_latent (RoPE always applied)
- * Each output is accumulated in fp32 (in 256-element chunks of d_model, the
- * chunks added in order) and rounded once to bf16; the row is then stored
+ * Each output is accumulated in fp32 (in 256-element chunks of d_model; the
+ * chunk sums are added in order within runs of four chunks, and the run sums
+ * in order) and rounded once to bf16; the row is then stored
  * exactly as mla_append_latent stores it.  Supported when d_c + d_rope is a
  * multiple of 32 (else MLA_ERR_UNSUPPORTED).  n_tokens == 0 is a no-op.
  */

@@ -189,7 +189,7 @@ bool project_supported(const mla_dims_t* d, int32_t d_model) {
          d_model <= (1 << 16);
 }
 size_t project_ws_bytes(const mla_dims_t* d, int32_t d_model, int32_t n_tokens) {
-  return sizeof(float) * static_cast<size_t>(d_model / mla::kDownChunk) * static_cast<size_t>(n_tokens) *
+  return sizeof(float) * static_cast<size_t>(mla::down_groups(d_model)) * static_cast<size_t>(n_tokens) *
          static_cast<size_t>(d->d_c + d->d_rope);
 }
 }  // namespace
@@ -241,7 +241,7 @@ mla_status_t mla_project_append(const mla_dims_t* d, int32_t d_model, const void
   a.rope = true;
   a.rope_base = d->rope_base;
   a.part = p.part;
-  a.n_part = d_model / mla::kDownChunk;
+  a.n_part = mla::down_groups(d_model);
   a.positions = positions;
   a.seq_ids = seq_ids;
   a.block_table = block_table;

@@ -33,14 +33,17 @@ struct AppendArgs {
   float* scales;
 };
 
-// Split-K down-projection of mla_project_append: part[ks][t][n] =
-// sum over d_model elements [kDownChunk ks, +kDownChunk) of h[t][k] w_down[n][k].
+// Split-K down-projection of mla_project_append: part[ks][t][n] = the sum,
+// in chunk order, of the fp32 sums over the 256-element chunks
+// kDownGroup ks .. kDownGroup ks + kDownGroup - 1 of h[t][k] w_down[n][k].
 constexpr int kDownChunk = 256;
+constexpr int kDownGroup = 4;                 // chunks per workgroup, summed in order
+constexpr int down_groups(int d_model) { return (d_model / kDownChunk + kDownGroup - 1) / kDownGroup; }
 struct ProjectArgs {
   int T, N, d_model;         // tokens, outputs (d_c + d_rope), reduction length
   const uint16_t* h;         // bf16 [T][d_model]
   const uint16_t* w_down;    // bf16 [N][d_model]
-  float* part;               // fp32 [d_model / kDownChunk][T][N]
+  float* part;               // fp32 [down_groups(d_model)][T][N]
 };
 
 struct AbsorbArgs {

@@ -255,7 +255,7 @@ def test_project_append_validation():
     f = lib.mla_project_append
     T, dm = 8, 7168
     need = lib.mla_project_append_workspace_size(ctypes.byref(d), dm, T)
-    assert need == 4 * (dm // 256) * T * 576
+    assert need == 4 * ((dm // 256 + 3) // 4) * T * 576   # fp32 partials, one per run of four 256-chunks
     assert lib.mla_project_append_workspace_size(ctypes.byref(d), 7000, T) == 0   # not a multiple of 256
     t = mla.make_dims(4, 32, 16, 16, 16, 16)                                     # 48-wide rows
     assert lib.mla_project_append_workspace_size(ctypes.byref(t), 256, T) == 0

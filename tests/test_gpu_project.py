@@ -3,10 +3,13 @@
 content of `cache_rows`; placement bit-exact (every other slot keeps its NaN
 poison).
 
-Bar: the projected c_kv values are the oracle's bf16 values or one bf16 step
-away (the GPU rounds an fp32 sum, the oracle the exact value; a value whose
-fp32 sum falls on the other side of a rounding midpoint moves by one step),
-with at most 1 % of them moved; the rotated key part meets the decode bar
+Bar: every projected c_kv value is within half a bf16 step plus the fp32
+summation bound ((d_model - 1) 2^-24 sum |h_k w_k|) of the exact value; where
+that bound is below half a step (all but outputs whose terms cancel to near
+zero) the value is the oracle's bf16 value or one bf16 step away (the GPU
+rounds an fp32 sum, the oracle the exact value; a value whose fp32 sum falls
+on the other side of a rounding midpoint moves by one step), with at most
+1 % of them moved and at most 0.1 % moved more; the rotated key part meets the decode bar
 (max |gpu - oracle| <= 2e-2, relative L2 <= 5e-3).  fp8 rows are compared
 code by code with the oracle's encoder applied to the oracle's bf16 rows: a
 value that moved one bf16 step can cross an fp8 rounding midpoint, so codes
@@ -68,8 +71,25 @@ def test_project_append_matches_oracle(case):
         want_c = c_bits.astype(np.int32)
         step = np.abs(got_c - want_c)
         same_sign = (got_c >> 15) == (want_c >> 15)
-        assert np.all((step == 0) | ((step == 1) & same_sign)), int(step.max())
+        # fp32 accumulation of d_model exact bf16 products, in any order, is
+        # within (d_model - 1) u sum |h_k w_k| (u = 2^-24) of the exact sum;
+        # rounding to bf16 adds half a step.  Where that error is below half
+        # a step the result is the exact value rounded (step <= 1); near-zero
+        # outputs, where the terms cancel, may be further off within it.
+        h64, w64 = bf16_bits_to_f64(pin.h), bf16_bits_to_f64(pin.w_down)
+        y = h64 @ w64.T
+        bound = (d_model - 1) * 2.0 ** -24 * (np.abs(h64) @ np.abs(w64).T)
+        got_v = bf16_bits_to_f64(rows[:, :wl.d_c])
+        err = np.abs(got_v - y[:, :wl.d_c])
+        # half a bf16 step at the larger of the two magnitudes: |x| in
+        # [2^(E-1), 2^E) has steps of 2^(E-8)
+        _, E = np.frexp(np.maximum(np.abs(got_v), np.abs(y[:, :wl.d_c])))
+        half_step = np.ldexp(1.0, E - 9)
+        assert np.all(err <= half_step + bound[:, :wl.d_c]), float(np.max(err - half_step - bound[:, :wl.d_c]))
+        well = bound[:, :wl.d_c] < half_step
+        assert np.all(((step == 0) | ((step == 1) & same_sign))[well]), int(step[well].max())
         assert np.mean(step) <= 1e-2, np.mean(step)
+        assert np.mean(step > 1) <= 1e-3, np.mean(step > 1)
         assert_close(bf16_bits_to_f64(rows[:, wl.d_c:]), Kr, "k_pe (rotated)")
         written = np.zeros(host.shape[:2], bool)
         written[pages, slots] = True
