@@ -58,9 +58,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kHeadroom = 64.0f;  // log2 units
 
 // MFMA operand reads kept in flight ahead of their MFMA: QK^T of the general
-// layout, and the specialised layout's K reads (each feeding two MFMAs)
+// layout, and the specialised layout's K reads (each feeding two MFMAs; a
+// second read in flight costs a spill reload per tile, and is slower)
 constexpr int kQkAhead = 4;
-constexpr int kQk2Ahead = 2;
+constexpr int kQk2Ahead = 1;
 
 template <int DC, int DR, int NW, bool FP8 = false>
 struct DecodeCfg {
