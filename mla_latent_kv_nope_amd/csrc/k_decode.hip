@@ -62,6 +62,7 @@ constexpr float kHeadroom = 64.0f;  // log2 units
 // second read in flight costs a spill reload per tile, and is slower)
 constexpr int kQkAhead = 4;
 constexpr int kQk2Ahead = 1;
+constexpr int kQk8Ahead = 2;   // (fp8 cache: 16-byte reads, each feeding four MFMAs)
 
 template <int DC, int DR, int NW, bool FP8 = false>
 struct DecodeCfg {
@@ -78,10 +79,10 @@ struct DecodeCfg {
   static constexpr int THREADS = 64 * NW;
   // tile loads are issued by the last LW waves (the others start computing
   // right after each barrier); loader i issues blocks i, i + LW, ...
-  // Specialised layout (d_c 512, d_rope 64, 8 waves, bf16 cache): waves 0-3
-  // score 32 heads each, waves 4-7 accumulate most of O and issue every tile
-  // copy (loader i copies the tile's 8-row group i).
-  static constexpr bool SPEC = NW == 8 && DC == 512 && DR == 64 && !FP8;
+  // Specialised layout (d_c 512, d_rope 64, 8 waves, bf16 or fp8 cache):
+  // waves 0-3 score 32 heads each, waves 4-7 accumulate most of O and issue
+  // every tile copy (bf16: loader i copies the tile's 8-row group i).
+  static constexpr bool SPEC = NW == 8 && DC == 512 && DR == 64;
   static constexpr int LW = SPEC ? 4 : NW;
   static constexpr int LD_HI = (INSTR + LW - 1) / LW;  // loads of loaders < INSTR % LW (or all)
   static constexpr int LD_LO = INSTR / LW;
@@ -94,22 +95,21 @@ struct DecodeCfg {
     while ((n + 1) * TILE_BYTES <= LDS_MAX && (n - 1) * LD_HI <= 63 && n < 4) ++n;
     return n;
   }
-  // fp8 cache: the bf16 ring keeps the two tiles in use (QK and PV); fp8 tiles
-  // (+ their 32 per-token scales) stream into a ring of SNB staging slots and
-  // are converted to bf16 between two barriers
-  static constexpr int NBUF = FP8 ? 2 : nbuf();
-  static constexpr int F8_TILE = kTile * R;             // bytes of an fp8 tile
-  static constexpr int F8_BLK = (F8_TILE + 1023) / 1024;
-  static constexpr int F8_SLOT = F8_TILE + 4 * kTile;   // + fp32 scales
-  static constexpr int SNB = 3;
-  static constexpr int STAGE_BYTES = FP8 ? SNB * F8_SLOT : 0;
-  static_assert(!FP8 || (BLOCKED && F8_TILE % 1024 == 0 && F8_SLOT % 128 == 0), "fp8 tile shape");
-  // rows of a tile in one 1 KB copy block never straddle the 16-row boundary
-  // (a tile spans two pages when pages hold 16 tokens)
-  static_assert(!FP8 || (16 * R) % 1024 == 0, "fp8 half tiles are whole copy blocks");
+  // fp8 cache (specialised layout only): the tiles stay fp8 in a ring of NBUF
+  // slots of F8S_SLOT bytes (nope blocks, rope blocks, then the 32 fp32
+  // scales; the layout is described at the copies)
+  static_assert(!FP8 || SPEC, "the fp8 cache runs in the specialised layout");
+  static constexpr bool SPEC8 = SPEC && FP8;
+  static constexpr int F8S_ROPE = kTile * DC;           // rope blocks after the 16 KB of nope blocks
+  static constexpr int F8S_SCL = kTile * R;             // scales after the two rope blocks
+  static constexpr int F8S_SLOT = (kTile * R + 4 * kTile + 1023) / 1024 * 1024;
+  static constexpr int NBUF = FP8 ? 7 : nbuf();
+  static constexpr int SLOT_BYTES = SPEC8 ? F8S_SLOT : TILE_BYTES;
   static_assert(R % 16 == 0 && DC % 16 == 0, "dims");
   static_assert((kTile * CPR) % 64 == 0, "tile load split");
-  static_assert((NBUF - 2) * LD_HI <= 63, "vmcnt range");
+  static_assert(SPEC8 || (NBUF - 2) * LD_HI <= 63, "vmcnt range");
+  static_assert(!SPEC8 || (DC == 16 * kTile && DR == 2 * kTile && (NBUF - 2) * 5 <= 63 && F8S_SLOT % 1024 == 0),
+                "fp8 slot: 16 nope blocks, 2 rope blocks, the scales; up to 5 copies per loader and tile");
   static_assert(!BLOCKED || TILE_BYTES % 1024 == 0, "blocked tiles keep the low 10 address bits free");
 };
 
@@ -135,15 +135,18 @@ __device__ __forceinline__ void wait_tiles(int pending) {
   wait_vmcnt<0>();
 }
 
-// waits until at most n (0 <= n, clamped to N) vector memory operations of
-// this wave are outstanding; n is wave-uniform
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if constexpr (N == 0) {
+// waits until at most `pending` (0 <= pending <= P, wave-uniform) groups of L
+// vector memory operations of this wave are outstanding
+template <int P, int L>
+__device__ __forceinline__ void wait_pending(int pending) {
+  if constexpr (P == 0) {
     wait_vmcnt<0>();
   } else {
-    if (n >= N) wait_vmcnt<N>();
-    else wait_vmcnt_le<N - 1>(n);
+    if (pending >= P) {
+      wait_vmcnt<P * L>();
+      return;
+    }
+    wait_pending<P - 1, L>(pending);
   }
 }
 
@@ -182,16 +185,12 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   static_assert(Cfg::VCB % NW == 0, "column blocks split evenly over the waves");
   static_assert(PROW == 64, "P rows are four 16-byte chunks");
   static_assert(!Cfg::BLOCKED || CPW % 4 == 0, "blocked PV reads start at a multiple of 4 column blocks");
-  // tile ring, (fp8: staging slots,) then two P slots (the second also
-  // carries the per-head 1/l at the end of a piece; the first the overflow vote)
-  // (fp8: then the per-token scales of the two bf16 tiles in use)
-  constexpr int SCL_BYTES = FP8 ? 2 * kTile * 4 : 0;
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::TILE_BYTES + Cfg::STAGE_BYTES + 2 * PSLOT + SCL_BYTES];
-  char* const stage = lds + Cfg::NBUF * Cfg::TILE_BYTES;
-  char* const pbuf = stage + Cfg::STAGE_BYTES;
+  // tile ring, then two P slots (the second also carries the per-head 1/l at
+  // the end of a piece; the first the overflow vote)
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::NBUF * Cfg::SLOT_BYTES + 2 * PSLOT];
+  char* const pbuf = lds + Cfg::NBUF * Cfg::SLOT_BYTES;
   int* const vote = reinterpret_cast<int*>(pbuf);
   float* const inv_share = reinterpret_cast<float*>(pbuf + PSLOT);
-  float* const scl = reinterpret_cast<float*>(pbuf + 2 * PSLOT);
 
   // Piece index of this workgroup.  Workgroups are dispatched round-robin
   // over the 8 XCDs (blockIdx % 8); consecutive pieces, which are mostly the
@@ -331,6 +330,20 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     qb.tail = Cfg::K16 ? lds_off<Cfg>(r, 4 * Cfg::K32 + (q & 1)) : 0u;
     return qb;
   };
+  // fp8 K operand reads (specialised layout): chunk 4m + quad of row 16tbk +
+  // l16 at even + 8192 tbk + 1024 (m / 2) when m % 2 == tbk, else at odd (the
+  // even base with chunk bit 2 flipped) + the same; rope chunk quad at rope +
+  // 1024 tbk past the nope blocks.
+  struct K8Bases { uint32_t even, odd, rope; };
+  auto k8_bases = [&]() -> K8Bases {
+    const int l = lane_id_fresh();
+    const int r = l & 15, q = l >> 4;
+    K8Bases kb;
+    kb.even = static_cast<uint32_t>(4096 * (r >> 3) + 128 * (r & 7) + 16 * (q ^ (r & 7)));
+    kb.odd = kb.even ^ 64u;
+    kb.rope = static_cast<uint32_t>(64 * r + 16 * (q ^ (r >> 2)));
+    return kb;
+  };
   // PV transpose reads: source lane 4r+q of its group reads row 4*quad + r (+16),
   // chunk 2cb + q/2, bytes 8*(q%2).  Blocked: the base for cb % 4 = m is the
   // base for m = 0 with chunk bits 1-2 xor m, plus 1 KB per cb/4; row-major:
@@ -437,7 +450,74 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         }
       }
     };
+    // ---- fp8 cache, specialised layout: the tile stays fp8 in its ring slot.
+    // Nope columns: 16 blocks of 1 KB, block 4rg + cg holding rows 8rg .. 8rg
+    // + 7 and 16-byte chunks 8cg .. 8cg + 7, chunk c of row t at byte 128(t %
+    // 8) + 16((c ^ sw(t)) % 8) with sw(t) = t % 8 ^ 4(t / 16 % 2).  Rope
+    // columns: 2 blocks of 16 rows x 4 chunks, chunk c of row t at 64(t % 16) +
+    // 16(c ^ (t / 4 % 4)).  Then the 32 fp32 scales.  Every 16-byte K operand
+    // read (8 lanes: 8 rows, one chunk) and every 8-bit transpose read of V
+    // (16 lanes: 8 rows of one chunk, rows t and t + 16 among them) falls on
+    // distinct banks.  Loader i copies column group i of the four row groups,
+    // then rope block i (i < 2) or the scales (i = 2): 5, 5, 5 and 4 copies.
+    // A row past the sequence (or on a page outside the pool) copies the same
+    // chunk of the tile's first row; masked scores take no scale.
+    auto issue_f8 = [&](int lt, int buf) {
+      if (loader < 0) return;
+      const int tok0 = lt * kTile;
+      const uint32_t dst = lds_addr(lds + buf * Cfg::SLOT_BYTES);
+      const uint8_t* const pool8 = static_cast<const uint8_t*>(a.pool);
+      const int64_t pb8 = static_cast<int64_t>(R) << lg;
+      const int pg0 = page_id(tok0);
+      const bool ok0 = pg0 >= 0 && pg0 < a.num_pages;
+      const uint8_t* row0 = ok0 ? pool8 + pg0 * pb8 + (tok0 & (ps - 1)) * R : pool8;
+      const int l = lane_id_fresh();
+      if (ps >= kTile && tok0 + kTile <= S && ok0) {
+        // one contiguous tile: scalar block base + the lane's fixed offset
+        const uint32_t ca = 16u * ((l & 7) ^ (l >> 3));
+        const uint32_t oa = (l >> 3) * R + ca, ob = (l >> 3) * R + (ca ^ 64u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          lds_dma16(row0 + 8 * j * R + 128 * loader, j < 2 ? oa : ob, dst + (4 * j + loader) * 1024);
+        if (loader < 2) {
+          const uint32_t orp = (l >> 2) * R + 512 + 16 * ((l & 3) ^ (l >> 4));
+          lds_dma16(row0 + 16 * loader * R, orp, dst + Cfg::F8S_ROPE + loader * 1024);
+        } else if (loader == 2 && l < kTile / 4) {
+          lds_dma16_v(a.scales + static_cast<int64_t>(pg0) * ps + (tok0 & (ps - 1)) + 4 * l, dst + Cfg::F8S_SCL);
+        }
+        return;
+      }
+      // rows 16 .. 31 lie on the next page when pages hold 16 tokens
+      const int pg1 = ps >= kTile ? pg0 : (tok0 + 16 < S ? page_id(tok0 + 16) : -1);
+      const bool ok1 = pg1 >= 0 && pg1 < a.num_pages;
+      auto row_src = [&](int t, int byte) -> const uint8_t* {
+        const bool hi = t >= 16;
+        const bool ok = ok0 && (hi ? ok1 : true) && tok0 + t < S;
+        return ok ? pool8 + (hi ? pg1 : pg0) * pb8 + ((tok0 + t) & (ps - 1)) * R + byte : row0 + byte;
+      };
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 8 * j + (l >> 3);
+        const int c = 8 * loader + ((l & 7) ^ (l >> 3) ^ (j < 2 ? 0 : 4));
+        lds_dma16_v(row_src(t, 16 * c), dst + (4 * j + loader) * 1024);
+      }
+      if (loader < 2) {
+        const int t = 16 * loader + (l >> 2);
+        lds_dma16_v(row_src(t, 512 + 16 * ((l & 3) ^ (l >> 4))), dst + Cfg::F8S_ROPE + loader * 1024);
+      } else if (loader == 2 && l < kTile / 4) {
+        const int t = 4 * l;                         // tokens t .. t + 3, one page
+        const bool hi = t >= 16;
+        const bool ok = ok0 && (hi ? ok1 : true) && tok0 + t < S;
+        const float* src = ok ? a.scales + static_cast<int64_t>(hi ? pg1 : pg0) * ps + ((tok0 + t) & (ps - 1))
+                              : (ok0 ? a.scales + static_cast<int64_t>(pg0) * ps + (tok0 & (ps - 1)) : a.scales);
+        lds_dma16_v(src, dst + Cfg::F8S_SCL);
+      }
+    };
     auto issue_tile = [&](int lt, int buf) {
+      if constexpr (Cfg::SPEC8) {
+        issue_f8(lt, buf);
+        return;
+      }
       const int tok0 = lt * kTile;
       char* dst_tile = lds + buf * Cfg::TILE_BYTES;
       if constexpr (Cfg::BLOCKED) {
@@ -477,89 +557,6 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       issue_general(tok0, dst_tile);
     };
 
-    // ---- fp8 cache.  Copies of one tile (R bytes per token) and its 32
-    // per-token scales into a staging slot.  Per lane: 16 bytes of row r; rows
-    // past the sequence, or on a page outside the pool, copy the tile's first
-    // row instead (and its scale), so converted rows are always finite.  A
-    // 1 KB copy block lies in one 16-row half of the tile, hence in one page.
-    const uint8_t* const pool8 = static_cast<const uint8_t*>(a.pool);
-    const int64_t page_bytes8 = static_cast<int64_t>(R) << lg;
-    // The NWV waves wv = 0 .. NWV - 1 share a tile's copies (the last one also
-    // copies the scales).
-    auto issue_tile8 = [&](int lt, int sslot, auto nwv_t, int wv) {
-      constexpr int NWV = decltype(nwv_t)::value;
-      const int tok0 = lt * kTile;
-      char* dst = stage + sslot * Cfg::F8_SLOT;
-      const int pg0 = page_id(tok0);
-      const int pg1 = ps >= kTile ? pg0 : page_id(tok0 + 16);
-      const bool ok0 = pg0 >= 0 && pg0 < a.num_pages;
-      const bool ok1 = pg1 >= 0 && pg1 < a.num_pages;
-      const uint8_t* row0 = ok0 ? pool8 + pg0 * page_bytes8 + (tok0 & (ps - 1)) * R : pool8;
-      const int l = lane_id_fresh();
-#pragma unroll
-      for (int j = 0; j < (Cfg::F8_BLK + NWV - 1) / NWV; ++j) {
-        const int blk = j * NWV + wv;
-        if (blk < Cfg::F8_BLK) {
-          const int b = blk * 1024 + 16 * l;
-          const int r = b / R, c = b - r * R;
-          const bool hi = r >= 16;
-          const int pg = hi ? pg1 : pg0;
-          const bool ok = (hi ? ok1 : ok0) && ok0 && tok0 + r < S;
-          const uint8_t* src = ok ? pool8 + pg * page_bytes8 + ((tok0 + r) & (ps - 1)) * R + c : row0 + c;
-          lds_dma16_v(src, lds_addr(dst + blk * 1024));
-        }
-      }
-      if (wv == NWV - 1 && l < kTile / 4) {        // scales of tokens 4l .. 4l + 3
-        const float* sc = a.scales;
-        const bool hi = 4 * l >= 16;
-        const int pg = hi ? pg1 : pg0;
-        const bool ok = (hi ? ok1 : ok0) && ok0 && tok0 + 4 * l < S;
-        const float* src = ok ? sc + static_cast<int64_t>(pg) * ps + ((tok0 + 4 * l) & (ps - 1))
-                              : (ok0 ? sc + static_cast<int64_t>(pg0) * ps + (tok0 & (ps - 1)) : sc);
-        lds_dma16_v(src, lds_addr(dst + Cfg::F8_TILE));
-      }
-    };
-    // vector memory operations copying wave wv of NWV issues per fp8 tile
-    auto ld8_of = [](int nwv, int wv) { return (Cfg::F8_BLK - wv + nwv - 1) / nwv + (wv == nwv - 1 ? 1 : 0); };
-    // staging slot -> bf16 ring slot: 8 codes (one bf16 chunk) per unit,
-    // converted exactly to bf16 by the gfx950 conversion instruction at scale
-    // 1, by the nwv waves wv = 0 .. nwv - 1 (units wv * 64 + lane + k * nwv *
-    // 64; the lane index is taken fresh so that no per-unit address is held
-    // across the tile loop); the tile's scales go to scl[bslot]
-    auto convert8 = [&](int lt, int sslot, int bslot, auto nwv_t, int wv) {
-      constexpr int NWV = decltype(nwv_t)::value;
-      constexpr int UPR = R / 8;                    // units per row
-      constexpr int NU = (kTile * UPR + 64 * NWV - 1) / (64 * NWV);   // units per lane
-      const int tok0 = lt * kTile;
-      const char* src = stage + sslot * Cfg::F8_SLOT;
-      const float* sls = reinterpret_cast<const float*>(src + Cfg::F8_TILE);
-      char* dst = lds + bslot * Cfg::TILE_BYTES;
-      const int u0 = wv * 64 + lane_id_fresh();
-      // every unit's codes are read first, then converted and written
-      uint2 x[NU];
-#pragma unroll
-      for (int k = 0; k < NU; ++k) {
-        const int u = u0 + k * 64 * NWV;
-        if (u < kTile * UPR) {
-          const int r = u / UPR, c = u - r * UPR;
-          x[k] = *reinterpret_cast<const uint2*>(src + r * R + 8 * c);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < NU; ++k) {
-        const int u = u0 + k * 64 * NWV;
-        if (u < kTile * UPR) {
-          const int r = u / UPR, c = u - r * UPR;
-          const uint4 y = {fp8x2_to_bf16x2<false>(x[k].x), fp8x2_to_bf16x2<true>(x[k].x),
-                           fp8x2_to_bf16x2<false>(x[k].y), fp8x2_to_bf16x2<true>(x[k].y)};
-          *reinterpret_cast<uint4*>(dst + lds_off<Cfg>(r, c)) = y;
-        }
-      }
-      // the tile's per-token scales, applied to its scores and to P (rows
-      // past the sequence, masked, take row 0's finite scale)
-      if (u0 < kTile) scl[bslot * kTile + u0] = tok0 + u0 < S ? sls[u0] : sls[0];
-    };
-
     if constexpr (Cfg::SPEC) {
     // ---- Specialised roles.  QK waves (0-3): S^T (32 tokens x 32 heads) as
     // two 16-head groups sharing every K operand read (K tile rows are the A
@@ -575,13 +572,21 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // leaves the registers for more)
     static_assert(HBC == 1 || HBC == NW, "head blocks computed: 1 or all");
     constexpr int NG = HBC == 1 ? 1 : 2;
-    constexpr int QD = NG == 1 ? 6 : kQk2Ahead;
+    constexpr int QD = NG == 1 ? 6 : (FP8 ? kQk8Ahead : kQk2Ahead);
     static_assert(NQW * QH == 16 * NW && NQW * QCB + (NW - NQW) * PCB == Cfg::VCB && Cfg::BLOCKED &&
                   Cfg::LW == NW - NQW && Cfg::INSTR % Cfg::LW == 0 && AHEAD >= 1, "specialised shape");
     const bool qkw = wave < NQW;
 
     auto sync_tile = [&](int it) {
-      if (!qkw) wait_tiles<AHEAD + 2, Cfg::LD_HI>(min(ntiles - 1 - it, AHEAD - 1));
+      if (!qkw) {
+        const int pending = min(ntiles - 1 - it, AHEAD - 1);
+        if constexpr (FP8) {
+          if (loader == 3) wait_pending<AHEAD - 1, 4>(pending);
+          else wait_pending<AHEAD - 1, 5>(pending);
+        } else {
+          wait_tiles<AHEAD + 2, Cfg::LD_HI>(pending);
+        }
+      }
       block_barrier();
     };
     // a score far above the offset anywhere in the workgroup: redo the piece
@@ -599,17 +604,43 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // O += P . V over all head blocks and column blocks [cbf, cbf + NC): B (V,
     // transpose reads) held for the wave's column blocks while the head
     // blocks' A operands (P rows) stream past, read AD head blocks ahead.
+    // fp8: one 8-bit transpose read per column block: source lane 2k + h of
+    // group `quad` reads row T = k < 4 ? 4quad + k : 16 + 4quad + k - 4 (the P
+    // k-slot order), bytes 8h .. 8h + 7 of chunk cb, and lane l16 receives
+    // column 16cb + l16 of the 8 rows; the codes convert exactly to bf16.
+    auto pv8_base = [&]() -> uint32_t {
+      const int l = lane_id_fresh();
+      const int q = l >> 4, k = (l & 15) >> 1, h = l & 1;
+      const int t = k < 4 ? 4 * q + k : 16 + 4 * q + k - 4;
+      const int sw = (t & 7) ^ (4 * (t >> 4));
+      return static_cast<uint32_t>(4096 * (t >> 3) + 128 * (t & 7) + 16 * sw + 8 * h);
+    };
     auto pv_cols = [&](const char* tb, int pslot, int cbf, auto& oo) {
       constexpr int NC = sizeof(oo[0]) / sizeof(oo[0][0]);
-      const uint32_t pb = pv_base0();
       bf16x8 vb[NC];
+      if constexpr (FP8) {
+        const uint32_t pb = pv8_base();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int cb = cbf + c;
-        const char* p0 = tb + ((pb ^ static_cast<uint32_t>(32 * (cb & 3))) + 1024 * (cb >> 2));
-        const bf16x4 v0 = lds_read_tr16(p0);
-        const bf16x4 v1 = lds_read_tr16(p0 + 16 * ROWB);
-        vb[c] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int c = 0; c < NC; ++c) {
+          const int cb = cbf + c;
+          // (the chunk xor touches address bits 4-6 only)
+          const v2i32 r = lds_read_tr8(tb + ((pb ^ static_cast<uint32_t>(16 * (cb & 7))) + 1024 * (cb >> 3)));
+          const uint4 y = {fp8x2_to_bf16x2<false>(static_cast<uint32_t>(r[0])),
+                           fp8x2_to_bf16x2<true>(static_cast<uint32_t>(r[0])),
+                           fp8x2_to_bf16x2<false>(static_cast<uint32_t>(r[1])),
+                           fp8x2_to_bf16x2<true>(static_cast<uint32_t>(r[1]))};
+          vb[c] = __builtin_bit_cast(bf16x8, y);
+        }
+      } else {
+        const uint32_t pb = pv_base0();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int cb = cbf + c;
+          const char* p0 = tb + ((pb ^ static_cast<uint32_t>(32 * (cb & 3))) + 1024 * (cb >> 2));
+          const bf16x4 v0 = lds_read_tr16(p0);
+          const bf16x4 v1 = lds_read_tr16(p0 + 16 * ROWB);
+          vb[c] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       }
       const char* pa_base = pbuf + pslot * PSLOT + p_lane_off();
       constexpr int AD = HBC < 3 ? HBC : 3;
@@ -647,7 +678,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       // groups (4 rows apart) start 64 bytes apart modulo the 256 bytes of one
       // pass over the banks.
       constexpr int ROWE = DC + 8;                             // elements per staged row
-      static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::TILE_BYTES, "row staging fits the ring");
+      static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::SLOT_BYTES, "row staging fits the ring");
       uint16_t* const st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
       for (int hb = 0; hb < HBC; ++hb) {
@@ -677,17 +708,19 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       // in the barriers and its (empty) share of O
       const bool scores = hq < 16 * HBC;
       // Q of NG 16-head groups g: lane holds head hq + 16g + l16, elements
-      // [32kc + 8quad, +8) of chunk kc
+      // [32kc + 8quad, +8) of chunk kc (bf16 cache), or [64(kc / 2) + 16quad +
+      // 8(kc % 2), +8) (fp8 cache: one 16-byte K read feeds chunks kc, kc + 1)
       bf16x8 qg[NG][Cfg::K32];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const int h = hq + 16 * g + l16;
         const bool hv = h < H;
-        const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * H + (hv ? h : 0)) * R + 8 * quad;
+        const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * H + (hv ? h : 0)) * R;
         const bf16x8 z = {};
 #pragma unroll
         for (int kc = 0; kc < Cfg::K32; ++kc) {
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * kc);
+          const int e = FP8 ? 64 * (kc >> 1) + 16 * quad + 8 * (kc & 1) : 32 * kc + 8 * quad;
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + e);
           qg[g][kc] = hv ? v : z;
         }
       }
@@ -707,24 +740,72 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       auto score2 = [&](const char* tb, int tok0, bool set_offset, int pslot) {
         auto body = [&](auto mask_t) {
           constexpr bool MASK = decltype(mask_t)::value;
-          const QkBases qb = qk_bases();
-          auto a_ptr = [&](int i) {
-            const int kc = i >> 1, tbk = i & 1;
-            return reinterpret_cast<const bf16x8*>(tb + ((kc & 1) ? qb.odd : qb.even) + tbk * 16 * ROWB +
-                                                   1024 * (kc >> 1));
-          };
-          constexpr int NQ = 2 * Cfg::K32;
           f32x4 sacc[NG][2] = {};
-          bf16x8 abuf[QD];
+          if constexpr (FP8) {
+            // 16-byte K reads j = 2m + tbk (row 16tbk + l16, chunk 4m + quad;
+            // m = 8 reads the rope chunk quad), each converted exactly into the
+            // bf16 A operands of chunks 2m and 2m + 1
+            const K8Bases kb = k8_bases();
+            auto k_ptr = [&](int j) {
+              const int m = j >> 1, tbk = j & 1;
+              const uint32_t off = m < 8 ? ((((m & 1) ^ tbk) ? kb.odd : kb.even) + 8192 * tbk + 1024 * (m >> 1))
+                                         : Cfg::F8S_ROPE + kb.rope + 1024 * tbk;
+              return reinterpret_cast<const uint4*>(tb + off);
+            };
+            constexpr int NR = Cfg::K32;
+            uint4 kbuf[QD];
 #pragma unroll
-          for (int i = 0; i < QD; ++i) abuf[i] = *a_ptr(i);
+            for (int i = 0; i < QD; ++i) kbuf[i] = *k_ptr(i);
 #pragma unroll
-          for (int i = 0; i < NQ; ++i) {
-            const bf16x8 av = abuf[i % QD];
-            if (i + QD < NQ) abuf[i % QD] = *a_ptr(i + QD);
+            for (int j = 0; j < NR; ++j) {
+              const uint4 kv = kbuf[j % QD];
+              if (j + QD < NR) kbuf[j % QD] = *k_ptr(j + QD);
+              const int m = j >> 1, tbk = j & 1;
+              const uint4 c0 = {fp8x2_to_bf16x2<false>(kv.x), fp8x2_to_bf16x2<true>(kv.x),
+                                fp8x2_to_bf16x2<false>(kv.y), fp8x2_to_bf16x2<true>(kv.y)};
+              const uint4 c1 = {fp8x2_to_bf16x2<false>(kv.z), fp8x2_to_bf16x2<true>(kv.z),
+                                fp8x2_to_bf16x2<false>(kv.w), fp8x2_to_bf16x2<true>(kv.w)};
 #pragma unroll
-            for (int g = 0; g < NG; ++g) sacc[g][i & 1] = mfma16(av, qg[g][i >> 1], sacc[g][i & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+              for (int g = 0; g < NG; ++g)
+                sacc[g][tbk] = mfma16(__builtin_bit_cast(bf16x8, c0), qg[g][2 * m], sacc[g][tbk]);
+#pragma unroll
+              for (int g = 0; g < NG; ++g)
+                sacc[g][tbk] = mfma16(__builtin_bit_cast(bf16x8, c1), qg[g][2 * m + 1], sacc[g][tbk]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            const QkBases qb = qk_bases();
+            auto a_ptr = [&](int i) {
+              const int kc = i >> 1, tbk = i & 1;
+              return reinterpret_cast<const bf16x8*>(tb + ((kc & 1) ? qb.odd : qb.even) + tbk * 16 * ROWB +
+                                                     1024 * (kc >> 1));
+            };
+            constexpr int NQ = 2 * Cfg::K32;
+            bf16x8 abuf[QD];
+#pragma unroll
+            for (int i = 0; i < QD; ++i) abuf[i] = *a_ptr(i);
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+              const bf16x8 av = abuf[i % QD];
+              if (i + QD < NQ) abuf[i % QD] = *a_ptr(i + QD);
+#pragma unroll
+              for (int g = 0; g < NG; ++g) sacc[g][i & 1] = mfma16(av, qg[g][i >> 1], sacc[g][i & 1]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // fp8: the score of token t is scale_t (q . code_t), and P carries
+          // scale_t into P . V (a masked token's scale, possibly never
+          // written, is not used: its P is zero and its scale taken as zero)
+          float sc[8];
+          if constexpr (FP8) {
+            const float* sp = reinterpret_cast<const float*>(tb + Cfg::F8S_SCL) + 4 * quad;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sc[i] = (!MASK || tok0 + 4 * quad + i < S) ? lo[i] : 0.f;
+              sc[4 + i] = (!MASK || tok0 + 16 + 4 * quad + i < S) ? hi[i] : 0.f;
+            }
           }
           const uint32_t poff = p_lane_off();
           // sacc[g][tbk][i] is token 16tbk + 4quad + i of head hq + 16g + l16
@@ -736,7 +817,8 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tbk + 4 * quad + i;
-                x[4 * tbk + i] = (!MASK || tok0 + t < S) ? sacc[g][tbk][i] : -INFINITY;
+                const float v = FP8 ? sacc[g][tbk][i] * sc[4 * tbk + i] : sacc[g][tbk][i];
+                x[4 * tbk + i] = (!MASK || tok0 + t < S) ? v : -INFINITY;
               }
             if (set_offset) {                       // first tile: O is still zero
               float mt = -INFINITY;
@@ -753,7 +835,8 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
               const float p0 = __builtin_amdgcn_exp2f(y0);
               const float p1 = __builtin_amdgcn_exp2f(y1);
               l_part[g] += p0 + p1;
-              pu[j] = pack_bf16x2(p0, p1);
+              if constexpr (FP8) pu[j] = pack_bf16x2(p0 * sc[2 * j], p1 * sc[2 * j + 1]);
+              else pu[j] = pack_bf16x2(p0, p1);
             }
             // P in PV A-operand order: k slot 8quad + j <-> token (j < 4 ? 4quad + j : 16 + 4quad + j - 4)
             *reinterpret_cast<bf16x8*>(pbuf + pslot * PSLOT + (hq + 16 * g) * PROW + poff) =
@@ -778,11 +861,11 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         score2(lds, lt0 * kTile, pass == 0, 0);
         for (int it = 1; it < ntiles; ++it) {
           sync_tile(it);
-          score2(lds + (it % Cfg::NBUF) * Cfg::TILE_BYTES, (lt0 + it) * kTile, false, it & 1);
-          pv_cols(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (it - 1) & 1, QCB * wave, oo);
+          score2(lds + (it % Cfg::NBUF) * Cfg::SLOT_BYTES, (lt0 + it) * kTile, false, it & 1);
+          pv_cols(lds + ((it - 1) % Cfg::NBUF) * Cfg::SLOT_BYTES, (it - 1) & 1, QCB * wave, oo);
         }
         block_barrier();
-        pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1, QCB * wave, oo);
+        pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::SLOT_BYTES, (ntiles - 1) & 1, QCB * wave, oo);
         const bool again = vote_again(y_max[0] > kHeadroom || y_max[1] > kHeadroom);
         if (!again || pass > 0) break;   // the second pass starts at the true maximum
 #pragma unroll
@@ -824,10 +907,10 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         for (int it = 1; it < ntiles; ++it) {
           sync_tile(it);
           if (it + AHEAD < ntiles) issue_tile(lt0 + it + AHEAD, (it + AHEAD) % Cfg::NBUF);
-          pv_cols(lds + ((it - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (it - 1) & 1, cbf, oo);
+          pv_cols(lds + ((it - 1) % Cfg::NBUF) * Cfg::SLOT_BYTES, (it - 1) & 1, cbf, oo);
         }
         block_barrier();
-        pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1, cbf, oo);
+        pv_cols(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::SLOT_BYTES, (ntiles - 1) & 1, cbf, oo);
         const bool again = vote_again(false);
         if (!again || pass > 0) break;
       }
@@ -876,13 +959,11 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // the previous tile, V from its still-resident ring slot).  Two ring slots
     // are read per iteration, so AHEAD = NBUF - 2 tiles are in flight; the one
     // barrier per tile both releases a ring slot and publishes P.
-    constexpr int AHEAD = FP8 ? 1 : Cfg::NBUF - 2;    // (the fp8 path stages its own tiles)
+    constexpr int AHEAD = Cfg::NBUF - 2;
     static_assert(AHEAD >= 1, "ring too small");
-    if constexpr (!FP8) {
 #pragma unroll
-      for (int i = 0; i < AHEAD; ++i)
-        if (i < ntiles) issue_tile(lt0 + i, i);
-    }
+    for (int i = 0; i < AHEAD; ++i)
+      if (i < ntiles) issue_tile(lt0 + i, i);
 
     // ---- S^T = K_tile . Q^T.  MFMA i covers chunk kc = i/2 of token block
     // tbk = i%2 (two independent accumulator chains, interleaved).  A operand =
@@ -927,26 +1008,8 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // ---- online softmax of one tile; sacc[tb][i] is token 16tb + 4*quad + i,
     // head l16.  Returns P as the PV A operand: k slot 8*quad + j <-> token
     // (j < 4 ? 4quad + j : 16 + 4quad + j - 4).
-    // fp8 cache: the tile holds the exact codes; the score of token t is
-    // scale_t * (q . code_t) and P carries scale_t into the P . V product
-    // (the tile's scales sit in scl[slot]).
-    auto softmax = [&](const f32x4* sacc, int tok0, bool set_offset, int slot) -> bf16x8 {
-      float sc[8];
-      if constexpr (FP8) {
-        const float* sp = scl + slot * kTile + 4 * quad;
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[i] = lo[i];
-          sc[4 + i] = hi[i];
-        }
-      }
-      auto xval = [&](int tbk, int i) -> float {
-        const float v = sacc[tbk][i];
-        if constexpr (FP8) return v * sc[4 * tbk + i];
-        return v;
-      };
+    auto softmax = [&](const f32x4* sacc, int tok0, bool set_offset) -> bf16x8 {
+      auto xval = [&](int tbk, int i) -> float { return sacc[tbk][i]; };
       float x[8];
       float mt;
       if (tok0 + kTile <= S) {                    // whole tile valid: no mask
@@ -982,8 +1045,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
         const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * j], a.scale_log2, -m_use));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * j + 1], a.scale_log2, -m_use));
         l_part += p0 + p1;
-        if constexpr (FP8) pu[j] = pack_bf16x2(p0 * sc[2 * j], p1 * sc[2 * j + 1]);
-        else pu[j] = pack_bf16x2(p0, p1);
+        pu[j] = pack_bf16x2(p0, p1);
       }
       return __builtin_bit_cast(bf16x8, pu);
     };
@@ -1058,11 +1120,10 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       if (qk_wave) {
         f32x4 sacc[2];
         qk(tb, sacc);
-        p_store(pslot, softmax(sacc, tok0, set_offset, pslot));
+        p_store(pslot, softmax(sacc, tok0, set_offset));
       }
     };
 
-    if constexpr (!FP8) {
     // first tile: QK + softmax (sets the exponent offset on the first pass);
     // then each step computes S(it), its softmax and P(it), and PV(it - 1)
     wait_and_sync(0);
@@ -1077,34 +1138,6 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     // last tile's PV (its ring slot is not refilled: no later loads)
     block_barrier();
     pv(lds + ((ntiles - 1) % Cfg::NBUF) * Cfg::TILE_BYTES, (ntiles - 1) & 1);
-    } else {
-    // fp8: tiles it+1 .. it+SNB are in the staging ring while step it runs;
-    // step it = barrier A (bf16 tile it and P(it-1) visible, staging slot of
-    // tile it free) -> copies of tile it+SNB -> S(it), P(it) -> PV(it-1) ->
-    // wait for tile it+1 -> barrier B (bf16 slot of tile it-1 and P(it) free /
-    // visible) -> convert tile it+1 into the bf16 slot of tile it-1
-    constexpr int SNB = Cfg::SNB;
-    const int ld8 = ld8_of(NW, wave);
-#pragma unroll
-    for (int i = 0; i < SNB; ++i)
-      if (i < ntiles) issue_tile8(lt0 + i, i, std::integral_constant<int, NW>{}, wave);
-    wait_vmcnt_le<2 * (Cfg::F8_BLK + 1)>(min(ntiles - 1, SNB - 1) * ld8);
-    block_barrier();
-    convert8(lt0, 0, 0, std::integral_constant<int, NW>{}, wave);
-    for (int it = 0; it < ntiles; ++it) {
-      block_barrier();
-      if (it + SNB < ntiles) issue_tile8(lt0 + it + SNB, it % SNB, std::integral_constant<int, NW>{}, wave);
-      score_tile(lds + (it & 1) * Cfg::TILE_BYTES, (lt0 + it) * kTile, pass == 0 && it == 0, it & 1);
-      if (it > 0) pv(lds + ((it - 1) & 1) * Cfg::TILE_BYTES, (it - 1) & 1);
-      if (it + 1 < ntiles) {
-        wait_vmcnt_le<2 * (Cfg::F8_BLK + 1)>((min(it + SNB, ntiles - 1) - (it + 1)) * ld8);
-        block_barrier();
-        convert8(lt0 + it + 1, (it + 1) % SNB, (it + 1) & 1, std::integral_constant<int, NW>{}, wave);
-      }
-    }
-    block_barrier();
-    pv(lds + ((ntiles - 1) & 1) * Cfg::TILE_BYTES, (ntiles - 1) & 1);
-    }
 
     // a score far above the offset anywhere in the workgroup: redo the piece
     // with each head's true maximum as its offset (cannot overflow again)
@@ -1248,7 +1281,8 @@ hipError_t launch_split_phase(const DecodeArgs& a, hipStream_t s, hipEvent_t ev0
   // not keep enough copies in flight (V2-Lite, H = 16: 145 us with one wave,
   // against a 9.5 us roofline).
   if (a.d_c == 512 && a.d_rope == 64 && a.fp8) {
-    e = launch_split<512, 64, 8, true>(a, s);
+    if (a.H <= 16) e = launch_split<512, 64, 8, true, 1>(a, s);
+    else e = launch_split<512, 64, 8, true>(a, s);
   } else if (a.fp8) {
     return hipErrorInvalidValue;
   } else if (a.d_c == 512 && a.d_rope == 64) {

@@ -11,6 +11,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int v2i32;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kWave = 64;
@@ -61,6 +62,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds_ptr) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(const_cast<void*>(lds_ptr)));
   return __builtin_bit_cast(bf16x4, v);
+}
+
+// 8-bit transpose read: in each 16-lane group, lane j receives byte j % 8 of
+// the 8 bytes addressed by lane 2k + j / 8 as its byte k (k = 0 .. 7): the
+// group's lanes address 8 rows of 16 bytes (two lanes per row) and each lane
+// gets one column of them.
+__device__ __forceinline__ v2i32 lds_read_tr8(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) v2i32*)(const_cast<void*>(lds_ptr)));
 }
 
 // ---- fp8 ------------------------------------------------------------------

@@ -349,7 +349,7 @@ def _piece_first_tiles(seq_lens, num_splits):
 
 @pytest.mark.parametrize("num_splits", [1, 5])
 def test_fp8_delta_query_redoes_piece_bit_exact(num_splits):
-    # fp8 cache (the general layout): each starred token lies past the first
+    # fp8 cache (specialised layout): each starred token lies past the first
     # tile of the piece holding it, so its score exceeds the piece's exponent
     # offset by far more than 64 (log2) and the piece is recomputed with the
     # true maximum; o_lat must still be the starred row exactly (code * 2^-6)
