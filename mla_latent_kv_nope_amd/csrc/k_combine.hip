@@ -13,7 +13,8 @@
 //
 // Partial slots (written by k_split): slot w + b of piece w of query sequence
 // b holds bf16 rows [16 ceil(H/16)][d_c] (normalised O) and fp32 lse [H].  The
-// pieces of sequence b are w = plan[b] / quota .. (plan[b + 1] - 1) / quota.
+// pieces of sequence b are w = (plan[b] + pc) / quota .. (plan[b + 1] - 1) /
+// quota, plan[] being cost positions and pc the per-sequence start cost.
 // Both kernels add the pieces in piece order in fp32, each weighted by
 // exp(lse_p - max lse), and divide by the sum of the weights.
 #include "mla_common.hpp"
@@ -27,9 +28,9 @@ struct PieceRange {
   int wf, np;
 };
 __device__ __forceinline__ PieceRange piece_range(const DecodeArgs& a, int b) {
-  const int t0 = a.plan[b], t1 = a.plan[b + 1], quota = a.plan[a.B + 1];
-  if (t1 == t0) return {0, 0};
-  const int wf = t0 / quota, wl = (t1 - 1) / quota;
+  const int c0 = a.plan[b], c1 = a.plan[b + 1], quota = a.plan[a.B + 1], pc = a.plan[a.B + 2];
+  if (c1 == c0) return {0, 0};
+  const int wf = (c0 + pc) / quota, wl = (c1 - 1) / quota;
   return {wf, wl - wf + 1};
 }
 

@@ -10,10 +10,11 @@
 //
 // This file holds the first of two kernels enqueued on the caller's stream:
 //   k_split   every workgroup first derives the plan (tiles per sequence,
-//             32 tokens each; quota = ceil(total tiles / parts)); workgroup w
-//             then takes global tiles [w*quota, (w+1)*quota) of the
-//             concatenated batch; a range may cover the tail of one sequence
-//             and the head of the next.  A piece that is a whole sequence
+//             32 tokens each, on a cost line that may charge each sequence a
+//             fixed start cost; quota = ceil(total cost / parts)); workgroup w
+//             then takes the tiles at cost positions [w*quota, (w+1)*quota)
+//             of the concatenated batch; a range may cover the tail of one
+//             sequence and the head of the next.  A piece that is a whole sequence
 //             writes o_lat/lse directly (unless o_lat is null); otherwise the
 //             piece's normalised O (bf16 rows [head][d_c]) and lse (fp32) go
 //             to slot w + b of the workspace.
@@ -33,15 +34,18 @@
 // LDS transpose read.  The softmax is base-2 with a per-head exponent offset
 // fixed by the piece's first tile; a piece whose scores later exceed it by
 // more than kHeadroom is recomputed once with the true maxima.
-//   General layout: every wave scores 16 heads (Q in 72 VGPRs; the head's row
-//        max is shared by four lanes) and accumulates O for all heads over
-//        its d_c / NW columns (128 accumulator registers at d_c 512).
-//   Specialised layout (d_c 512, d_rope 64, NW 8, bf16 cache): waves 0-3
-//        score 32 heads each, every K operand read feeding the MFMAs of two
-//        16-head groups (Q in 144 VGPRs, four independent accumulator
+//   General layout (the tiny dims): every wave scores 16 heads (Q in 72
+//        VGPRs; the head's row max is shared by four lanes) and accumulates
+//        O for all heads over its d_c / NW columns.
+//   Specialised layout (d_c 512, d_rope 64, NW 8, bf16 or fp8 cache): waves
+//        0-3 score 32 heads each, every K operand read feeding the MFMAs of
+//        two 16-head groups (Q in 144 VGPRs, four independent accumulator
 //        chains), and accumulate O for 2 column blocks; waves 4-7 accumulate
 //        O for 6 column blocks each and issue all tile copies, so the
-//        copies' issue stalls never hold up the scoring waves.
+//        copies' issue stalls never hold up the scoring waves.  An fp8 cache
+//        stays fp8 in LDS: the scoring waves convert their K reads to bf16 in
+//        registers, and V reaches the P.V MFMAs through 8-bit transpose
+//        reads; the per-token scale multiplies the scores and P.
 #include <atomic>
 #include <type_traits>
 
@@ -56,6 +60,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // 2^kHeadroom (far inside fp32 and bf16 range) unless a score exceeds the
 // offset by more than that; such a piece is recomputed with its true maximum.
 constexpr float kHeadroom = 64.0f;  // log2 units
+
+// What starting one more piece inside a workgroup's range costs, in tiles
+// (the query load, the ring's refill and the partial store; measured about
+// 3-4 tiles of steady-state work): the plan charges it per sequence when the
+// batch's lengths differ.
+constexpr int kPieceCost = 4;
 
 // MFMA operand reads kept in flight ahead of their MFMA: QK^T of the general
 // layout, and the specialised layout's K reads (each feeding two MFMAs; a
@@ -212,12 +222,20 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // ---- plan, computed by every workgroup: tiles per sequence, the total,
-  // quota = ceil(total / parts) and the first (sequence, tile offset) of this
-  // workgroup's range [w * quota, (w + 1) * quota).  Thread i sums a chunk of
-  // C consecutive sequences; a wave scan plus the wave totals (in the P slots,
-  // unused until the first tile) give each chunk's first tile.  Workgroup 0
-  // also stores the prefix sums and the quota for the merge kernels.
+  // ---- plan, computed by every workgroup.  The batch is a cost line: each
+  // non-empty sequence costs its tiles plus pc (0 or kPieceCost) before its
+  // first tile; quota = ceil(total cost / parts) and workgroup w takes the
+  // tiles at cost positions [w * quota, (w + 1) * quota).  With ragged
+  // lengths some workgroups' ranges hold several sequence starts, each one
+  // more piece to run, and pc = kPieceCost spreads that cost; when every
+  // non-empty sequence has the same tile count, pc = 0 (ranges then fall on
+  // sequence starts or hold at most one, and a charge would only shift tiles
+  // between workgroups).  Thread i sums the tiles and non-empty sequences of
+  // a chunk of C consecutive sequences (and notes whether their tile counts
+  // differ); wave scans plus the wave totals (in the P slots, unused until
+  // the first tile) give each chunk's first position.  Workgroup 0 also
+  // stores the cost prefix sums, the total, the quota and pc for the merge
+  // kernels.
   // Query sequence v is new token qi = v % q_len of cache sequence cs =
   // v / q_len and sees len_of(cs, qi) tokens (the cache sequence's length less
   // its later new tokens).  (cs, qi) pairs are walked incrementally: one
@@ -235,11 +253,30 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
   const int C = (B + Cfg::THREADS - 1) / Cfg::THREADS;
   const int k0 = static_cast<int>(threadIdx.x) * C;
   const int cs0 = k0 / QL, qi0 = k0 - cs0 * QL;   // query sequence k0
-  int csum = 0;
-  {
+  // Tiles of query sequence k0 + j of the chunk (walked as (cs, qi)); the plan
+  // needs them in up to three passes.  With one sequence per thread (B <= 512,
+  // the usual case) the length is loaded once, here, and no pass loops.
+  const bool one = C == 1;
+  const int n_one = (one && k0 < B) ? tiles_len(len_of(cs0, qi0)) : 0;
+  int csum = 0, cne = 0;                        // tiles, non-empty sequences
+  int n_first = -1;                             // tile count of the first non-empty one
+  bool differs = false;                         // another one unlike it
+  if (one) {
+    csum = n_one;
+    cne = n_one > 0;
+    n_first = n_one > 0 ? n_one : -1;
+  } else {
     int cs = cs0, qi = qi0;
     for (int j = 0; j < C; ++j, next_query(cs, qi))
-      if (k0 + j < B) csum += tiles_len(len_of(cs, qi));
+      if (k0 + j < B) {
+        const int n = tiles_len(len_of(cs, qi));
+        csum += n;
+        cne += n > 0;
+        if (n > 0) {
+          differs |= n_first >= 0 && n != n_first;
+          if (n_first < 0) n_first = n;
+        }
+      }
   }
   int incl = csum;
 #pragma unroll
@@ -247,50 +284,94 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     const int v = __shfl_up(incl, d);
     if (lane >= d) incl += v;
   }
-  if (lane == 63) scan[wave] = incl;
+  // the wave's reference: the first lane holding a non-empty sequence
+  const uint64_t has = __builtin_amdgcn_ballot_w64(n_first >= 0);
+  const int ref = has != 0 ? __builtin_amdgcn_readlane(n_first, __builtin_ctzll(has)) : -1;
+  differs |= n_first >= 0 && n_first != ref;
+  const bool wave_differs = __builtin_amdgcn_ballot_w64(differs) != 0;
+  if (lane == 63) {
+    scan[wave] = incl;
+    scan[NW + wave] = wave_differs;
+    scan[2 * NW + wave] = ref;
+  }
   __syncthreads();
-  int total = 0, before = 0;
+  int total = 0, before = 0, ragged = 0, ref_all = -1;
   for (int i = 0; i < NW; ++i) {
-    const int v = scan[i];
+    const int v = scan[i], r = scan[2 * NW + i];
     total += v;
+    ragged |= scan[NW + i] | (r >= 0 && ref_all >= 0 && r != ref_all);
+    if (ref_all < 0) ref_all = r;
     if (i < wave) before += v;
   }
   const int excl = before + incl - csum;       // tiles before this thread's chunk
-  const int quota = total > 0 ? (total + a.num_parts - 1) / a.num_parts : 1;
+  const int pc = ragged ? kPieceCost : 0;
+  // cost positions: with a start cost, the non-empty sequences before each
+  // chunk are counted too (a second scan, in words of its own)
+  int total_c = total, excl_c = excl;
+  if (pc != 0) {
+    int incl_n = cne;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl_n, d);
+      if (lane >= d) incl_n += v;
+    }
+    if (lane == 63) scan[3 * NW + wave] = incl_n;
+    __syncthreads();
+    int total_n = 0, before_n = 0;
+    for (int i = 0; i < NW; ++i) {
+      const int v = scan[3 * NW + i];
+      total_n += v;
+      if (i < wave) before_n += v;
+    }
+    total_c += pc * total_n;
+    excl_c += pc * (before_n + incl_n - cne);
+  }
+  const int quota = total_c > 0 ? (total_c + a.num_parts - 1) / a.num_parts : 1;
+  auto cost_of = [&](int n) { return n > 0 ? n + pc : 0; };
   if (w == 0) {
-    int p0 = excl;
-    int cs = cs0, qi = qi0;
-    for (int j = 0; j < C; ++j, next_query(cs, qi))
-      if (k0 + j < B) {
-        plan[k0 + j] = p0;
-        p0 += tiles_len(len_of(cs, qi));
-      }
+    if (one) {
+      if (k0 < B) plan[k0] = excl_c;
+    } else {
+      int p0 = excl_c;
+      int cs = cs0, qi = qi0;
+      for (int j = 0; j < C; ++j, next_query(cs, qi))
+        if (k0 + j < B) {
+          plan[k0 + j] = p0;
+          p0 += cost_of(tiles_len(len_of(cs, qi)));
+        }
+    }
     if (threadIdx.x == 0) {
-      plan[B] = total;
+      plan[B] = total_c;
       plan[B + 1] = quota;
+      plan[B + 2] = pc;
     }
   }
   int g = w * quota;
-  const int gend = min(g + quota, total);
+  const int gend = min(g + quota, total_c);
   if (g >= gend) return;
   __syncthreads();                              // wave totals read before reuse
-  // the chunk holding tile g names the sequence containing it
-  if (excl <= g && g < excl + csum) {
-    int p0 = excl;
-    int cs = cs0, qi = qi0;
-    for (int j = 0; j < C; ++j, next_query(cs, qi)) {
-      const int n = k0 + j < B ? tiles_len(len_of(cs, qi)) : 0;
-      if (g < p0 + n) {
-        scan[0] = k0 + j;
-        scan[1] = p0;
-        break;
+  // the chunk holding cost position g names the sequence containing it
+  if (excl_c <= g && g < excl_c + csum + pc * cne) {
+    if (one) {
+      scan[0] = k0;
+      scan[1] = excl_c;
+    } else {
+      int p0 = excl_c;
+      int cs = cs0, qi = qi0;
+      for (int j = 0; j < C; ++j, next_query(cs, qi)) {
+        const int n = k0 + j < B ? cost_of(tiles_len(len_of(cs, qi))) : 0;
+        if (g < p0 + n) {
+          scan[0] = k0 + j;
+          scan[1] = p0;
+          break;
+        }
+        p0 += n;
       }
-      p0 += n;
     }
   }
   __syncthreads();
   int b = scan[0];
-  int t0 = scan[1];                             // first tile of sequence b
+  int t0 = scan[1];                             // cost position where sequence b starts
   int b_cs = b / QL, b_qi = b - b_cs * QL;      // its cache sequence and new-token index
   const int quad = lane >> 4;          // k slice (operands) / token quad (S) / head quad (O)
   const int l16 = lane & 15;
@@ -374,13 +455,16 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
 
   while (g < gend) {
     const int S = len_of(b_cs, b_qi);
-    const int t1 = t0 + tiles_len(S);
-    const int lt0 = g - t0, lt1 = min(gend, t1) - t0;
+    const int nt = tiles_len(S);
+    const int first = t0 + pc;                  // cost position of its first tile
+    const int t1 = first + nt;
+    const int lt0 = max(g - first, 0), lt1 = min(gend, t1) - first;
+    if (lt1 <= lt0) break;                      // the range ends before the sequence's first tile
     const int ntiles = lt1 - lt0;
     // a piece that is a whole sequence writes o_lat / lse itself, unless the
     // caller merges every piece afterwards (o_lat null: merged with the
     // output projection)
-    const bool whole = a.o_lat != nullptr && (lt0 == 0) && (lt1 == t1 - t0);
+    const bool whole = a.o_lat != nullptr && (lt0 == 0) && (lt1 == nt);
     const int32_t* bt = block_table + static_cast<int64_t>(b_cs) * a.max_pages;
     const char* pool = static_cast<const char*>(a.pool);
     const int64_t page_bytes = static_cast<int64_t>(ROWB) << lg;
@@ -1210,7 +1294,7 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
     }  // general path
 
     // next piece: the next non-empty sequence
-    g = t0 + lt1;
+    g = first + lt1;
     t0 = t1;
     ++b;
     next_query(b_cs, b_qi);
@@ -1264,7 +1348,7 @@ WorkspaceLayout decode_workspace_layout(int B, int H, int d_c, int num_parts) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   WorkspaceLayout L;
   L.plan_off = 0;
-  L.part_o_off = up(sizeof(int32_t) * (static_cast<size_t>(B) + 2));
+  L.part_o_off = up(sizeof(int32_t) * (static_cast<size_t>(B) + 3));
   const size_t slots = static_cast<size_t>(num_parts) + B;
   const size_t hpad = (static_cast<size_t>(H) + 15) / 16 * 16;
   L.part_lse_off = L.part_o_off + up(sizeof(uint16_t) * slots * hpad * d_c);

@@ -64,7 +64,8 @@ struct OutProjArgs {
 };
 
 // Workspace of mla_decode_paged, carved from the caller's buffer:
-//   plan      int32 [B + 1] tile prefix sums, then int32 quota
+//   plan      int32 [B + 1] cost-line prefix sums (tiles, plus pc before
+//             each non-empty sequence), then int32 quota and int32 pc
 //   part_o    bf16 [num_parts + B][16 ceil(H/16)][d_c]  normalised partial
 //             outputs, one row per head
 //   part_lse  fp32 [num_parts + B][H]

@@ -339,12 +339,66 @@ def _delta_query(wl):
     return q
 
 
-def _piece_first_tiles(seq_lens, num_splits):
-    """Global tile index where each piece of the split plan starts."""
+PIECE_COST = 4   # tiles the split plan charges per sequence start, when it charges one
+
+
+def _split_plan(seq_lens, num_splits):
+    """The split plan as the merge kernels read it: cost-line prefix sums per
+    sequence (tiles, plus pc before each non-empty sequence), the total cost,
+    the quota and pc.  pc is PIECE_COST exactly when the non-empty
+    sequences' tile counts differ."""
     tiles = [(s + 31) // 32 for s in seq_lens]
-    total = sum(tiles)
-    quota = -(-total // num_splits)
-    return {w * quota for w in range(num_splits) if w * quota < total}
+    pc = PIECE_COST if len({n for n in tiles if n > 0}) > 1 else 0
+    cost = [n + pc if n > 0 else 0 for n in tiles]
+    prefix = np.concatenate([[0], np.cumsum(cost)])
+    total_c = int(prefix[-1])
+    quota = -(-total_c // num_splits) if total_c > 0 else 1
+    return prefix[:-1].astype(np.int64), total_c, quota, pc
+
+
+def _piece_first_tiles(seq_lens, num_splits):
+    """Global tile index (over the concatenated batch) where each piece of
+    the split plan starts."""
+    tiles = [(s + 31) // 32 for s in seq_lens]
+    first_tile = np.concatenate([[0], np.cumsum(tiles)])
+    prefix, total_c, quota, pc = _split_plan(seq_lens, num_splits)
+    out = set()
+    for w in range(num_splits):
+        x = w * quota
+        if x >= total_c:
+            break
+        s = max(i for i in range(len(seq_lens)) if prefix[i] <= x and tiles[i] > 0)
+        out.add(int(first_tile[s] + max(x - prefix[s] - pc, 0)))
+    return out
+
+
+@pytest.mark.parametrize("seq_lens,num_splits,want_pc", [
+    ((2048,) * 8, 8, 0),                    # equal lengths: no start cost
+    ((300, 1000, 4096, 77), 5, PIECE_COST),  # ragged: every start charged
+    ((0, 70, 0, 64, 0), 3, PIECE_COST),      # empty sequences cost nothing
+    ((0, 64, 0, 60, 0, 33), 3, 0),          # equal tile counts, empty ones between
+    ((4096,) * 3, 8, 0),
+])
+def test_split_plan_cost_line(seq_lens, num_splits, want_pc):
+    # the plan the split kernel stores for the merge kernels (workspace head:
+    # int32 [B] cost prefix sums, total, quota, pc), against its definition
+    wl = configs.V3.with_(name="v3_plan", batch=len(seq_lens), seq_len=None, seq_lens=seq_lens)
+    print(f"[decode plan] seq_lens={seq_lens} splits={num_splits}", flush=True)
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    B = len(seq_lens)
+    ws = mla.new_workspace(d, B, num_splits, DEV)
+    ws.zero_()
+    q = bf16_tensor(np.zeros((B, wl.n_heads, wl.d_c + wl.d_rope), np.uint16), DEV)
+    mla.decode_paged(d, q, pool, scales, t["block_table"], t["seq_lens"], num_splits=num_splits,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    got = ws[: 4 * (B + 3)].cpu().numpy().view(np.int32)
+    prefix, total_c, quota, pc = _split_plan(seq_lens, num_splits)
+    assert pc == want_pc
+    assert np.array_equal(got[:B], prefix), (got[:B], prefix)
+    assert (got[B], got[B + 1], got[B + 2]) == (total_c, quota, pc)
 
 
 @pytest.mark.parametrize("num_splits", [1, 5])
