@@ -271,9 +271,11 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t B, int32_t num_
  *   pool        cache as written by mla_append_latent; scales for fp8 else NULL
  *   block_table int32 [B][max_pages]
  *   seq_lens    int32 [B]: tokens of each sequence (0 allowed)
- *   num_splits  number of equal shares the batch's tokens are cut into, each
- *               processed by one workgroup (a share may span sequences, a
- *               sequence may span shares); 0 = automatic (fills the GPU)
+ *   num_splits  number of equal shares the batch is cut into, each processed
+ *               by one workgroup (a share may span sequences, a sequence may
+ *               span shares); shares are equal in 32-token tiles, plus a
+ *               fixed cost of 4 tiles per sequence start when the sequences'
+ *               tile counts differ; 0 = automatic (fills the GPU)
  *   workspace   device buffer of at least mla_decode_workspace_size() bytes,
  *               256-byte aligned; contents need no initialisation
  *   o_lat       bf16 [B][H][d_c] (written): sum_t p_t c_kv[t]
