@@ -12,15 +12,15 @@
 // token at position seq_lens[b] - n_b + i and attends to positions <= its own.
 //
 // Two kernels:
-//   k_up       one workgroup of four waves per (head, 1024 tokens), launched
-//              once for K and once for V: the head's [512 x 128] weight sits
-//              in LDS and is read with the gfx950 transpose read; each wave
-//              computes 64 tokens x 128 columns (two 32-token blocks sharing
-//              every weight operand), its latent rows going from the paged
-//              pool straight into MFMA registers in four quarters of the
-//              reduction, the next quarter loading while this quarter's
-//              MFMAs run; an fp8 cache's codes become bf16 (code * scale) at
-//              the MFMA.  K_nope is written [h][t][128] and V transposed
+//   k_up       one workgroup of eight waves (two per SIMD) per (head, 1024
+//              tokens), launched once for K and once for V: the head's
+//              [512 x 128] weight sits in LDS and is read with the gfx950
+//              transpose read; each wave computes 64 tokens x 128 columns
+//              (two 32-token blocks sharing every weight operand), its latent
+//              rows going from the paged pool straight into MFMA registers in
+//              eight parts of the reduction, the next part loading while this
+//              part's MFMAs run; an fp8 cache's codes become bf16 (code *
+//              scale) at the MFMA.  K_nope is written [h][t][128] and V transposed
 //              per 32-token tile, [h][t / 32][128][32] (the MFMA operands are
 //              swapped for V), so a key tile of one head is one contiguous
 //              8 KB run in each; the head-0 workgroups of the K launch
@@ -87,8 +87,12 @@ __device__ __forceinline__ uint32_t pair_transpose(float x0, float x1, int odd) 
 // ---------------------------------------------------------------------------
 // Up-projection
 // ---------------------------------------------------------------------------
+// kUpWaves waves per workgroup (two per SIMD), the reduction in kUpParts
+// parts of 512 / kUpParts elements
+constexpr int kUpWaves = 8, kUpParts = 8;
+
 template <bool IS_V, bool FP8>
-__global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kUpWaves) void k_up(PrefillArgs a) {
   constexpr int WROW = kPfDh * 2;                             // bytes per weight row
   __shared__ __attribute__((aligned(1024))) char wl[kPfDc * WROW];   // 128 KB
   const int h = blockIdx.x;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
   // W[h] [512][128]: chunk c of row k stored at c ^ 2 (k mod 4), so a
   // transpose read's 16-lane group touches 4 rows in distinct banks
   const uint16_t* wsrc = (IS_V ? a.w_uv : a.w_uk) + static_cast<int64_t>(h) * kPfDc * kPfDh;
-  for (int k = wave; k < kPfDc / 4; k += 4) {
+  for (int k = wave; k < kPfDc / 4; k += kUpWaves) {
     const int r = 4 * k + (lane >> 4);
     const int c = (lane & 15) ^ (2 * (r & 3));
     lds_dma16_v(wsrc + r * kPfDh + 8 * c, lds_addr(wl + 1024 * k));
@@ -134,20 +138,21 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
     }
   };
   // each wave takes two 32-token blocks, so every weight operand read from
-  // LDS feeds two MFMAs; the reduction runs in four 128-element quarters
-  // through two alternating register sets, the next quarter's loads in
-  // flight during this quarter's MFMAs (the row pointers are formed once per
-  // block, so no wait for a page id ever waits for those loads)
-  constexpr int kStride = 4 * 64;                              // tokens per pass of the workgroup
-  Raw qa[2][8], qb[2][8];
+  // LDS feeds two MFMAs; the reduction runs in kUpParts parts through two
+  // alternating register sets, the next part's loads in flight during this
+  // part's MFMAs (the row pointers are formed once per block, so no wait for
+  // a page id ever waits for those loads)
+  constexpr int kStride = kUpWaves * 64;                       // tokens per pass of the workgroup
+  constexpr int KS = kPfDc / 16 / kUpParts;                    // 16-element steps per part
+  Raw qa[2][KS], qb[2][KS];
   int64_t prow[2] = {0, 0};
   float sc[2] = {1.f, 1.f};
-  auto load_q = [&](Raw (*dst)[8], int qq) {
+  auto load_q = [&](Raw (*dst)[KS], int qq) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const char* base = row_ptr(prow[rb]);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) dst[rb][s] = *reinterpret_cast<const Raw*>(base + (128 * qq + 16 * s) * ES);
+      for (int s = 0; s < KS; ++s) dst[rb][s] = *reinterpret_cast<const Raw*>(base + (16 * KS * qq + 16 * s) * ES);
     }
   };
   auto set_rows = [&](int tq) {
@@ -169,16 +174,28 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
     const int64_t prow_now[2] = {prow[0], prow[1]};
     const float sc_now[2] = {sc[0], sc[1]};
     f32x16 acc[2][4] = {};
-    auto compute_q = [&](const Raw (*av)[8], int qq) {
+    // the lane's part of each weight read address, per 32-column tile ct
+    // (row 8 half + rr, the swizzled column chunk), formed here from a fresh
+    // lane id so that it is not hoisted out of the loop: every read is one of
+    // these four plus an immediate
+    uint32_t wlane[4];
+    {
+      const int fl = lane_id_fresh();
+      const int fhalf = fl >> 5, fG = fl >> 4, frr = (fl & 15) >> 2, fq = fl & 3;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int row = 16 * (8 * qq + s) + 8 * half + rr;      // row % 4 == rr
+      for (int ct = 0; ct < 4; ++ct) {
+        const int col0 = 32 * ct + 16 * (fG & 1) + 4 * fq;
+        wlane[ct] = static_cast<uint32_t>((8 * fhalf + frr) * WROW + ((col0 >> 3) ^ (2 * frr)) * 16 + (col0 & 7) * 2);
+      }
+    }
+    auto compute_q = [&](const Raw (*av)[KS], int qq) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int row0 = 16 * (KS * qq + s);                   // + 8 half + rr in wlane
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const int col0 = 32 * ct + 16 * (G & 1) + 4 * q;
-          const int cb = ((col0 >> 3) ^ (2 * rr)) * 16 + (col0 & 7) * 2;
-          const bf16x4 lo = lds_read_tr16(wl + row * WROW + cb);
-          const bf16x4 hi = lds_read_tr16(wl + (row + 4) * WROW + cb);
+          const bf16x4 lo = lds_read_tr16(wl + wlane[ct] + row0 * WROW);
+          const bf16x4 hi = lds_read_tr16(wl + wlane[ct] + (row0 + 4) * WROW);
           const bf16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
@@ -187,19 +204,24 @@ __global__ __launch_bounds__(256) void k_up(PrefillArgs a) {
             else acc[rb][ct] = mfma32(x, bv, acc[rb][ct]);
           }
         }
+        // (one 16-element step at a time: weight reads are not hoisted over
+        // later steps, which would hold their operands in registers)
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    load_q(qb, 1);
-    compute_q(qa, 0);
-    load_q(qa, 2);
-    compute_q(qb, 1);
-    load_q(qb, 3);
-    compute_q(qa, 2);
-    if (t0 + kStride < tend) {
-      set_rows(t0 + kStride);
-      load_q(qa, 0);
+    static_assert(kUpParts % 2 == 0, "parts alternate between the two register sets");
+#pragma unroll
+    for (int qq = 0; qq < kUpParts; qq += 2) {
+      load_q(qb, qq + 1);
+      compute_q(qa, qq);
+      if (qq + 2 < kUpParts) {
+        load_q(qa, qq + 2);
+      } else if (t0 + kStride < tend) {
+        set_rows(t0 + kStride);
+        load_q(qa, 0);
+      }
+      compute_q(qb, qq + 1);
     }
-    compute_q(qb, 3);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int tblk = t0 + 32 * rb;
@@ -538,11 +560,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, hipEvent_t up0, h
   const int ytiles = (a.s_cap + kUpTokens - 1) / kUpTokens;
   if (up0) (void)hipEventRecord(up0, s);
   if (a.fp8) {
-    hipLaunchKernelGGL((k_up<false, true>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_up<true, true>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_up<false, true>), dim3(a.H, ytiles, a.B), dim3(64 * kUpWaves), 0, s, a);
+    hipLaunchKernelGGL((k_up<true, true>), dim3(a.H, ytiles, a.B), dim3(64 * kUpWaves), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_up<false, false>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_up<true, false>), dim3(a.H, ytiles, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_up<false, false>), dim3(a.H, ytiles, a.B), dim3(64 * kUpWaves), 0, s, a);
+    hipLaunchKernelGGL((k_up<true, false>), dim3(a.H, ytiles, a.B), dim3(64 * kUpWaves), 0, s, a);
   }
   if (up1) (void)hipEventRecord(up1, s);
   if (at0) (void)hipEventRecord(at0, s);
