@@ -405,7 +405,7 @@ def main():
         cpu_baseline_all()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; the decode path shards by sequence "
+        print("bench.py: measures exactly one GPU; the decode path shards by sequence "
               "(attention data parallel) and needs no collective, but multi-GPU runs are not "
               "part of it. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
