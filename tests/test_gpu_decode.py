@@ -401,6 +401,47 @@ def test_split_plan_cost_line(seq_lens, num_splits, want_pc):
     assert (got[B], got[B + 1], got[B + 2]) == (total_c, quota, pc)
 
 
+@pytest.mark.parametrize("batch,num_splits,fp8", [
+    (700, 0, False), (700, 97, False), (1100, 300, False), (700, 97, True)])
+def test_more_sequences_than_plan_threads(batch, num_splits, fp8):
+    # more query sequences than the split kernel's 512 threads: each plan
+    # thread walks a chunk of ceil(B / 512) sequences (prefix sums, start
+    # costs, the search for a piece's first sequence), with empty sequences
+    # inside the chunks
+    rng = np.random.default_rng(batch + num_splits)
+    lens = rng.integers(1, 161, size=batch)
+    wl = configs.V2LITE.with_(name=f"v2lite_b{batch}", fp8=fp8, batch=batch, seq_len=None,
+                              seq_lens=tuple(int(x) for x in lens))
+    print(f"[decode many] B={batch} splits={num_splits} fp8={fp8}", flush=True)
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    q = mla.absorb_q(d, t["q_nope"], t["q_pe"], t["q_pos"], t["w_uk"])
+    run_lens = lens.astype(np.int32)
+    run_lens[::37] = 0
+    ws = mla.new_workspace(d, batch, num_splits, DEV)
+    o_lat, lse = mla.decode_paged(d, q, pool, scales, t["block_table"], i32_tensor(run_lens, DEV),
+                                  num_splits=num_splits, workspace=ws)
+    torch.cuda.synchronize()
+    head = ws[: 4 * (batch + 3)].cpu().numpy().view(np.int32)
+    prefix, total_c, quota, pc = _split_plan(tuple(int(x) for x in run_lens), max(num_splits, 1))
+    assert pc == PIECE_COST
+    assert np.array_equal(head[:batch], prefix)
+    assert (head[batch], head[batch + 2]) == (total_c, pc)
+    if num_splits > 0:
+        assert head[batch + 1] == quota
+    o = o_lat.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy()
+    empty = np.flatnonzero(run_lens == 0)
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
+    # sequences at the edges of the plan threads' chunks and of the batch
+    pick = [b for b in sorted({1, 2, 3, 255, 256, 511, 512, 513, batch - 2, batch - 1})
+            if run_lens[b] > 0]
+    ref = reference_decode(inp, batches=pick)
+    assert_close(o[pick], ref["o_lat"], "o_lat")
+    assert np.max(np.abs(l[pick] - ref["lse"])) <= 1e-2
+
+
 @pytest.mark.parametrize("num_splits", [1, 5])
 def test_fp8_delta_query_redoes_piece_bit_exact(num_splits):
     # fp8 cache (specialised layout): each starred token lies past the first
