@@ -43,7 +43,7 @@ CASES = [
 ]
 
 
-def run_prefill(inp, d, n_new=None, cache=None):
+def run_prefill(inp, d, n_new=None, cache=None, events=None):
     """Packs the last n_new[b] of each sequence's q_len new tokens and runs the
     call; returns host out [T][H][d_v], lse [T][H] and the row offsets."""
     wl = inp.wl
@@ -57,7 +57,7 @@ def run_prefill(inp, d, n_new=None, cache=None):
     starts = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
     q_start = torch.from_numpy(starts).to("cuda")
     out, lse = mla.prefill_paged(d, qn_p, qp_p, q_start, max(n_new), pool, scales,
-                                 t["block_table"], t["seq_lens"], t["w_uk"], t["w_uv"])
+                                 t["block_table"], t["seq_lens"], t["w_uk"], t["w_uv"], events=events)
     torch.cuda.synchronize()
     f = lambda x: x.float().cpu().numpy().astype(np.float64)
     return f(out), f(lse), starts, (pool, scales, t)
