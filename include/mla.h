@@ -33,9 +33,11 @@
  *   - Values that live on the device (seq_lens, block-table entries,
  *     positions, seq_ids) are not checked on the host.  Kernels treat
  *     out-of-range values defensively instead of faulting: a page id outside
- *     [0, num_pages) or a position beyond the block table is skipped (its
- *     token is neither written nor attended to) and seq_lens are clamped to
- *     [0, max_pages * page_size].  Results for such inputs are unspecified.
+ *     [0, num_pages) is never dereferenced (the append skips the token, as it
+ *     does a position beyond the block table; the attention kernels read a
+ *     row inside the pool in its place) and seq_lens are clamped to
+ *     [0, max_pages * page_size].  Results for the sequences concerned are
+ *     unspecified; other sequences of the call are unaffected.
  *   - Outputs must not alias inputs.  Calls on different streams that write
  *     the same buffers race.
  *
