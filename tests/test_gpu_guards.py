@@ -4,7 +4,8 @@ must not dereference them, and every other sequence of the call must come out
 bit for bit as in a call with a clean table.  The corrupted sequence's result
 is unspecified and not checked.  Covers the decode tile copies (bf16 whole
 tiles and 16-token pages, the fp8 tiles and their scales) and the prefill
-up-projection's row reads."""
+up-projection's row reads.  Also: seq_lens outside [0, max_pages * page_size]
+decode exactly as the clamped lengths."""
 import numpy as np
 import pytest
 import torch
@@ -66,3 +67,32 @@ def test_prefill_pages_outside_the_pool(fp8):
     rows = slice(int(starts[1]), int(starts[2]))          # sequence 1's new tokens
     assert np.array_equal(out0[rows], out1[rows])
     assert np.array_equal(lse0[rows], lse1[rows])
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_decode_seq_lens_are_clamped(fp8, num_splits):
+    # seq_lens are clamped to [0, max_pages * page_size]: -3 decodes as an empty
+    # sequence and cap + 500 as cap, bit for bit
+    wl = configs.V3.with_(name="v3_clamp", fp8=fp8, batch=3, seq_len=None, seq_lens=(64, 2048, 100))
+    print(f"[guards clamp] fp8={fp8} splits={num_splits}", flush=True)
+    inp = make_inputs(wl)
+    d = dims_for(wl)
+    pool, scales, t = build_cache(inp, d)
+    cap = inp.block_table.shape[1] * wl.page_size
+    assert cap == 2048
+    q = mla.absorb_q(d, t["q_nope"], t["q_pe"], t["q_pos"], t["w_uk"])
+    clean = i32_tensor(np.array([0, cap, 100], np.int32), "cuda")
+    wild = i32_tensor(np.array([-3, cap + 500, 100], np.int32), "cuda")
+    r = [mla.decode_paged(d, q, pool, scales, t["block_table"], s, num_splits=num_splits) for s in (clean, wild)]
+    p = [mla.decode_paged_out(d, q, pool, scales, t["block_table"], s, t["w_uv"], num_splits=num_splits,
+                              want_o_lat=True, want_lse=True) for s in (clean, wild)]
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(r[0][0]), bf16_bits(r[1][0]))
+    assert np.array_equal(r[0][1].cpu().numpy(), r[1][1].cpu().numpy())
+    for a, b in zip(p[0], p[1]):
+        if a.dtype == torch.bfloat16:
+            assert np.array_equal(bf16_bits(a), bf16_bits(b))
+        else:
+            assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+    assert np.all(bf16_bits(r[1][0])[0] == 0) and np.all(np.isneginf(r[1][1].cpu().numpy()[0]))
