@@ -764,15 +764,32 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       constexpr int ROWE = DC + 8;                             // elements per staged row
       static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::SLOT_BYTES, "row staging fits the ring");
       uint16_t* const st = reinterpret_cast<uint16_t*>(lds);
+      // bf16 cache: heads 4fq + i and 4fq + i + 1 of a column rounded as one
+      // pair (one conversion instruction), stored as two halves.  The fp8
+      // layout keeps the rounding one value at a time: with the pairs its
+      // scoring waves reload three spilled registers per tile instead of one.
 #pragma unroll
       for (int hb = 0; hb < HBC; ++hb) {
         if (hb < HB) {
+          if constexpr (FP8) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int h = hb * 16 + 4 * fq + i;
+            for (int i = 0; i < 4; ++i) {
+              const int h = hb * 16 + 4 * fq + i;
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-              st[h * ROWE + 16 * (cbf + c) + f16] = f32_to_bf16_bits(oo[hb][c][i]);
+              for (int c = 0; c < NC; ++c)
+                st[h * ROWE + 16 * (cbf + c) + f16] = f32_to_bf16_bits(oo[hb][c][i]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const int h = hb * 16 + 4 * fq + i;
+#pragma unroll
+              for (int c = 0; c < NC; ++c) {
+                const uint32_t pk = pack_bf16x2(oo[hb][c][i], oo[hb][c][i + 1]);
+                st[h * ROWE + 16 * (cbf + c) + f16] = static_cast<uint16_t>(pk);
+                st[(h + 1) * ROWE + 16 * (cbf + c) + f16] = static_cast<uint16_t>(pk >> 16);
+              }
+            }
           }
         }
       }
