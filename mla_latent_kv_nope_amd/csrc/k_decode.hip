@@ -764,14 +764,15 @@ void k_split(DecodeArgs a, int32_t* __restrict__ plan, const int32_t* __restrict
       constexpr int ROWE = DC + 8;                             // elements per staged row
       static_assert(16 * NW * ROWE * 2 <= Cfg::NBUF * Cfg::SLOT_BYTES, "row staging fits the ring");
       uint16_t* const st = reinterpret_cast<uint16_t*>(lds);
-      // bf16 cache: heads 4fq + i and 4fq + i + 1 of a column rounded as one
-      // pair (one conversion instruction), stored as two halves.  The fp8
-      // layout keeps the rounding one value at a time: with the pairs its
-      // scoring waves reload three spilled registers per tile instead of one.
+      // heads 4fq + i and 4fq + i + 1 of a column rounded as one pair (one
+      // conversion instruction), stored as two halves.  The fp8 layout's
+      // scoring waves (two column blocks) keep the rounding one value at a
+      // time: with the pairs there they reload three spilled registers per
+      // tile instead of one.
 #pragma unroll
       for (int hb = 0; hb < HBC; ++hb) {
         if (hb < HB) {
-          if constexpr (FP8) {
+          if constexpr (FP8 && NC == QCB) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int h = hb * 16 + 4 * fq + i;
